@@ -1,0 +1,208 @@
+"""Benchmark of the owner-side Muon step on one MI355X.
+
+One step = dmuon_step over the whole owned set (momentum, Newton-Schulz,
+update) with inputs resident in HBM.  Default workload: the 28-layer stack of
+the 3B decoder shapes (196 matrices, 2.82 G elements, bf16 params and grads,
+fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload 2] [--ns-backend gram]
+                  [--ns-precision bf16] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NS TFLOP/s and optimizer steps/s for a 3B-shaped owner set; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--ns-backend", default="gram", choices=["gram", "direct"])
+    ap.add_argument("--ns-precision", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", default="auto",
+                    help="'auto' (one matrix of each distinct shape) or 'none'")
+    return ap.parse_args()
+
+
+def nominal_flops(shapes, ns_steps):
+    tot = 0.0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        tot += ns_steps * (4.0 * m * m * n + 2.0 * m ** 3)
+    return tot
+
+
+def cpu_baseline(w, hp, budget_s=30.0):
+    """The oracle timed on this host: one step of one matrix of each distinct
+    shape (inputs from the seeded generator), extrapolated to the workload by
+    shape counts."""
+    import numpy as np
+    import dmuon_inputs as di
+    from oracle import muon as orc
+    shapes = {}
+    for i, m in enumerate(w.matrices):
+        shapes.setdefault((m.rows, m.cols), []).append(i)
+    per_shape = {}
+    t_start = time.time()
+    sampled = 0
+    for (r, c), idx in sorted(shapes.items(), key=lambda kv: kv[0][0] * kv[0][1]):
+        i = idx[0]
+        _, wexact = di.param_init(w, i)
+        _, g = di.grad_at(w, i, 0)
+        t0 = time.perf_counter()
+        orc.muon_step(wexact, g, np.zeros_like(g), lr=hp["lr"], momentum=hp["momentum"],
+                      nesterov=hp["nesterov"], ns_steps=hp["ns_steps"],
+                      weight_decay=hp["weight_decay"], ns_backend=hp["ns_backend"],
+                      param_dtype=w.param_dtype)
+        per_shape[(r, c)] = time.perf_counter() - t0
+        sampled += 1
+        if time.time() - t_start > budget_s:
+            break
+    if len(per_shape) < len(shapes):
+        # extrapolate the unsampled shapes by nominal flops of the sampled ones
+        rate = sum(nominal_flops([s], hp["ns_steps"]) for s in per_shape) / sum(per_shape.values())
+        for s in shapes:
+            per_shape.setdefault(s, nominal_flops([s], hp["ns_steps"]) / rate)
+    t_step = sum(per_shape[s] * len(idx) for s, idx in shapes.items())
+    flops = nominal_flops([(m.rows, m.cols) for m in w.matrices], hp["ns_steps"])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads),
+        "kind": "oracle",
+        "steps_per_s": 1.0 / t_step, "matrices_per_s": len(w.matrices) / t_step,
+        "sample": (f"float64 numpy oracle, one step of one matrix of each of the "
+                   f"{len(shapes)} distinct shapes ({sampled} timed, "
+                   f"{sum(per_shape[s] for s in per_shape if s in per_shape):.1f} s), "
+                   f"extrapolated to {len(w.matrices)} matrices by shape counts"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the owner step runs on one device with no "
+              f"collectives; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+
+    dev = torch.device("cuda:0")
+    w = di.workload(args.workload)
+    hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
+    shapes = [(m.rows, m.cols) for m in w.matrices]
+    pdt = torch.bfloat16 if w.param_dtype == "bf16" else torch.float32
+    gdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
+
+    # inputs resident in HBM: params, momenta, and one gradient set per step
+    params = []
+    for i, (r, c) in enumerate(shapes):
+        t = torch.empty(r, c, dtype=pdt, device=dev)
+        di.torch_normal_(t, w.param_std, seed=1000 + i)
+        params.append(t)
+    moms = [torch.zeros(r, c, dtype=torch.float32, device=dev) for r, c in shapes]
+    n_grad_sets = min(args.steps + args.warmup, 4)
+    grad_sets = []
+    for s in range(n_grad_sets):
+        gs = []
+        for i, (r, c) in enumerate(shapes):
+            t = torch.empty(r, c, dtype=gdt, device=dev)
+            di.torch_normal_(t, w.grad_std, seed=100000 * (s + 1) + i)
+            gs.append(t)
+        grad_sets.append(gs)
+    ws_bytes = dm.dmuon_step_workspace_size(params, grad_sets[0], moms, **hp)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    print(f"# workload {w.name}: {len(shapes)} matrices, {w.numel / 1e9:.3f} G elements, "
+          f"workspace {ws_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    for s in range(args.warmup):
+        dm.dmuon_step(params, grad_sets[s % n_grad_sets], moms, workspace=workspace, **hp)
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    dm.dmuon_profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        dm.dmuon_step(params, grad_sets[(args.warmup + s) % n_grad_sets], moms, workspace=workspace, **hp)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = dm.dmuon_profile_end()["kernels"]
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    flops_step = nominal_flops(shapes, hp["ns_steps"])
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if args.ns_precision == "bf16" else PEAK_F32_TFLOPS
+    gemm = {k: v for k, v in prof.items() if k.startswith("gemm")}
+    ns_ms = sum(v["ms"] for v in gemm.values()) / args.steps
+    exec_flops = sum(v["flops"] for v in gemm.values()) / args.steps
+    dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    kernels = {k: {"launches_per_step": v["launches"] / args.steps,
+                   "ms_per_step": v["ms"] / args.steps,
+                   "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
+                   "gbs": v["bytes"] / (v["ms"] * 1e-3) / 1e9}
+               for k, v in prof.items()}
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.ns_precision,
+        "data": "synthetic (seeded normal params and grads, generated on device)",
+        "config": {"workload": w.name, "matrices": len(shapes), "elements": w.numel,
+                   "ns_backend": args.ns_backend, "ns_precision": args.ns_precision,
+                   "ns_steps": hp["ns_steps"], "param_dtype": w.param_dtype,
+                   "grad_dtype": w.grad_dtype, "momentum_dtype": "f32"},
+        "steps_per_s": 1e3 / ms_step,
+        "matrices_per_s": len(shapes) * 1e3 / ms_step,
+        "ns_tflops_nominal": flops_step / (ns_ms * 1e-3) / 1e12,
+        "ns_executed_tflops": exec_flops / (ns_ms * 1e-3) / 1e12,
+        "ns_executed_frac_of_peak": exec_flops / (ns_ms * 1e-3) / 1e12 / peak,
+        "ns_ms_per_step": ns_ms,
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, hp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

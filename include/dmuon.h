@@ -1,0 +1,205 @@
+/*
+ * dmuon.h -- C ABI of the owner-side Muon step for MI355X (gfx950).
+ *
+ * The operation is the step that the DMuon Training Guide ("Step 4: Create
+ * Optimizer") assigns to the owner of each dedicated matrix parameter:
+ * momentum, then Newton-Schulz orthogonalisation, then the update.  The FAQ
+ * ("Why isn't DMuon just ZeRO-1?") explains why it runs on whole (m, n)
+ * matrices on one rank.  The hyperparameters and their defaults are the
+ * Training Guide's dmuon.Muon arguments and its "Hyperparameter Guide" table:
+ *   lr 0.02 (scaled per matrix by 0.2*sqrt(max(m, n))), momentum 0.95,
+ *   nesterov true (NS input = grad + momentum*buf), ns_steps 5,
+ *   weight_decay 0.0, ns_backend "gram" (default) or "direct".
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major and contiguous, rows x cols as stored.
+ *   - Pointers named "device" are device memory of the current HIP device;
+ *     the library reads and writes them only from kernels enqueued on
+ *     `stream` (a hipStream_t; NULL is the default stream).  Host structs
+ *     and arrays passed in are read before the call returns.
+ *   - The caller owns every buffer, including the workspace.  No entry point
+ *     allocates or frees device memory.  (The library keeps a small pinned
+ *     host staging ring and a shape-keyed plan cache for its own launch
+ *     tables.)
+ *   - Calls are asynchronous: results are visible to later work on `stream`.
+ *     Calls that share a workspace must be ordered on one stream.
+ *   - Return value: DMUON_OK, or a negative status.  Every argument check runs
+ *     before the first launch, so on an error status nothing was modified.
+ *     dmuon_last_error() gives a readable detail for the calling thread.
+ *   - Gradient values are not checked: a NaN or Inf in one matrix's gradient
+ *     propagates into that matrix only.
+ *   - Threads: entry points may be called from several host threads; calls
+ *     enqueued on different streams must use different workspaces.
+ */
+#ifndef DMUON_H
+#define DMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMUON_ABI_VERSION 1
+
+/* status codes */
+#define DMUON_OK                  0
+#define DMUON_ERR_INVALID_ARG    (-1)  /* NULL pointer, bad size, bad hyperparameter */
+#define DMUON_ERR_UNSUPPORTED    (-2)  /* dtype combination or device not supported   */
+#define DMUON_ERR_WORKSPACE      (-3)  /* workspace NULL or smaller than required     */
+#define DMUON_ERR_ALIASING       (-4)  /* two buffers overlap (the Training Guide's
+                                          "Semantic Param Groups" rejects duplicate
+                                          parameters the same way)                    */
+#define DMUON_ERR_HIP            (-5)  /* a HIP runtime call or launch failed          */
+
+typedef enum { DMUON_F32 = 0, DMUON_BF16 = 1 } dmuon_dtype_t;
+
+/* Training Guide, Hyperparameter Guide table, ns_backend row. */
+typedef enum { DMUON_NS_GRAM = 0, DMUON_NS_DIRECT = 1 } dmuon_ns_backend_t;
+
+/* Arithmetic of the NS products: bf16 operands with fp32 accumulation, or
+ * fp32 operands with fp32 accumulation. */
+typedef enum { DMUON_NS_PREC_BF16 = 0, DMUON_NS_PREC_F32 = 1 } dmuon_ns_prec_t;
+
+/* One owned matrix (the Training Guide's DedicatedParam, owner side). */
+typedef struct {
+  int64_t rows, cols;      /* as stored; both > 0                                 */
+  void* param;             /* device, rows*cols of param_dtype, updated in place  */
+  const void* grad;        /* device, rows*cols of grad_dtype; NULL skips the
+                              matrix for this step (nothing of it is touched)     */
+  float* momentum;         /* device, rows*cols fp32 momentum buffer, in/out;
+                              zero before the first step                          */
+  int32_t param_dtype;     /* dmuon_dtype_t */
+  int32_t grad_dtype;      /* dmuon_dtype_t */
+} dmuon_matrix_t;
+
+/* Hyperparameters of one parameter group (Training Guide, Step 4 and the
+ * Hyperparameter Guide table).  Use one call per group. */
+typedef struct {
+  double lr;               /* 0.02; the update is scaled by lr*0.2*sqrt(max(rows,cols)) */
+  double momentum;         /* 0.95                                                 */
+  int32_t nesterov;        /* 1: NS input = grad + momentum*buf (buf after its
+                              update); 0: NS input = buf                          */
+  int32_t ns_steps;        /* 5; 0..16                                             */
+  double weight_decay;     /* 0.0; decoupled: W <- W*(1 - lr*weight_decay) first    */
+  int32_t ns_backend;      /* dmuon_ns_backend_t, default DMUON_NS_GRAM            */
+  int32_t ns_precision;    /* dmuon_ns_prec_t, default DMUON_NS_PREC_BF16          */
+  const double* ns_coeffs; /* host; NULL: (3.4445, -4.7750, 2.0315) every step;
+                              else ns_coeffs_len values: one (a, b, c) triple for
+                              every step, or ns_steps triples (per-step table),
+                              the dmuon.NewtonSchulz(...) custom-coefficient case */
+  int32_t ns_coeffs_len;   /* 0, 3 or 3*ns_steps                                   */
+  double eps;              /* 1e-7, added to the Frobenius norm of the NS input    */
+} dmuon_hparams_t;
+
+/* Fill *hp with the Training Guide's defaults (and eps 1e-7, bf16 NS). */
+void dmuon_hparams_default(dmuon_hparams_t* hp);
+
+/*
+ * The whole step for a batch of n owned matrices (Training Guide, Step 4:
+ * "momentum + NS + update, owner only"):
+ *   buf <- momentum*buf + grad
+ *   U   <- grad + momentum*buf  (nesterov) | buf
+ *   X0  <- U / (||U||_F + eps), taken in the wide orientation (transposed
+ *          when rows > cols)
+ *   O   <- ns_steps Newton-Schulz iterations of X0 (direct or Gram form),
+ *          oriented back to rows x cols
+ *   W   <- W*(1 - lr*weight_decay) - lr*0.2*sqrt(max(rows,cols))*O, rounded
+ *          once (to nearest even) to the parameter dtype.
+ * Supported dtypes: param fp32 or bf16; grad fp32 or bf16; momentum fp32.
+ * `workspace` (device, >= dmuon_step_workspace_size bytes, 256-byte aligned)
+ * holds the NS intermediates; its contents on entry do not matter.
+ * Matrices with the same shape need not be adjacent; each matrix is
+ * independent of the others.  n == 0 is a no-op.
+ */
+size_t dmuon_step_workspace_size(const dmuon_matrix_t* mats, int32_t n,
+                                 const dmuon_hparams_t* hp);
+int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The momentum stage alone (the Hyperparameter Guide's momentum and nesterov
+ * rows): updates every matrix's momentum buffer in place and writes the NS
+ * input U of matrix i to ns_input[i] (device), dense and row-major in the wide
+ * orientation: min(rows,cols) x max(rows,cols), i.e. transposed when
+ * rows > cols, in ns_input_dtype (fp32 or bf16, rounded to nearest even).
+ * sumsq (device, n doubles) receives sum(U*U) of the fp32 values before any
+ * rounding.  The parameters are not read or written.  Matrices with a NULL
+ * grad are skipped (their ns_input and sumsq entries are left untouched).
+ * `workspace` (device, >= dmuon_momentum_workspace_size bytes) holds the
+ * launch table and the per-block partial sums.
+ */
+size_t dmuon_momentum_workspace_size(const dmuon_matrix_t* mats, int32_t n);
+int dmuon_momentum(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                   void* const* ns_input, int32_t ns_input_dtype, double* sumsq,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Newton-Schulz alone: out[i] = NS(in[i]) for n matrices of rows[i] x cols[i]
+ * (host arrays), with in/out device buffers of io_dtype (fp32 or bf16) in the
+ * stored orientation.  Uses hp->ns_steps, ns_backend, ns_precision,
+ * ns_coeffs and eps; the momentum and update fields are ignored.
+ * The backend "gram" runs the Gram form (FAQ, "What related work should I
+ * cite?": Gram Newton-Schulz) on matrices with max(rows,cols) >= 2*min(rows,
+ * cols) and the direct form on squarer ones, where the two cost the same and
+ * the Gram form loses accuracy in bf16; dmuon_backend_info() states the rule.
+ * in and out may be the same buffer.
+ */
+size_t dmuon_orthogonalize_workspace_size(const int64_t* rows, const int64_t* cols,
+                                          int32_t n, const dmuon_hparams_t* hp);
+int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* rows,
+                        const int64_t* cols, int32_t n, int32_t io_dtype,
+                        const dmuon_hparams_t* hp, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * The update stage alone: W <- W*(1 - lr*weight_decay) -
+ * lr*0.2*sqrt(max(rows,cols))*O for every matrix (Hyperparameter Guide, lr
+ * row; weight_decay of Step 4), with O = update[i] (device, rows x cols as
+ * stored, update_dtype fp32 or bf16).  Reads mats[i].param, rows, cols and
+ * param_dtype only; grad and momentum are ignored.  `workspace` (device,
+ * >= dmuon_apply_update_workspace_size bytes) holds the launch table.
+ */
+size_t dmuon_apply_update_workspace_size(int32_t n);
+int dmuon_apply_update(const dmuon_matrix_t* mats, int32_t n, const void* const* update,
+                       int32_t update_dtype, const dmuon_hparams_t* hp, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Readable name of a status code (static storage). */
+const char* dmuon_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* dmuon_last_error(void);
+
+/* Kernels, tile shapes and the Gram/direct rule, as a static string (the
+ * analog of the Training Guide's dmuon.get_ns_backend()). */
+const char* dmuon_backend_info(void);
+
+/*
+ * Measurement hooks.  Between dmuon_profile_begin() and dmuon_profile_end(),
+ * every kernel the library enqueues (from any entry point, on its stream) is
+ * bracketed by a pair of HIP events.  dmuon_profile_end() waits for those
+ * events and writes JSON into buf (as dmuon_plan_describe does): per kernel
+ * kind the launch count, summed device time in ms, and the algorithmic flops
+ * and HBM bytes of those launches (flops of the NS products with the true,
+ * unpadded sizes and symmetric products counted once; bytes that an ideal
+ * kernel must move).  Returns the JSON length or a negative status.  Called
+ * again with no profiling window open, it returns the last report (so a
+ * caller can size a buffer first).
+ * Profiling adds a few microseconds per launch; it is off by default.
+ */
+int dmuon_profile_begin(void);
+int64_t dmuon_profile_end(char* buf, size_t buf_len);
+
+/* Host-only: the launch plan dmuon_step would use for these shapes (NS form
+ * per matrix, workspace bytes, launches and tile counts), written as JSON into
+ * buf (NUL-terminated, truncated to buf_len).  Returns the full length needed
+ * (excluding the NUL), or a negative status.  Touches no device. */
+int64_t dmuon_plan_describe(const int64_t* rows, const int64_t* cols, int32_t n,
+                            const dmuon_hparams_t* hp, char* buf, size_t buf_len);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DMUON_H */

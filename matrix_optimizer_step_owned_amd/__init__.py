@@ -1,0 +1,344 @@
+"""Python binding of the dmuon C ABI (include/dmuon.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors
+are PyTorch tensors (device memory and streams come from PyTorch); all the
+arithmetic of the step runs in the library's HIP kernels.  The library must
+have been built (``__graft_entry__.build()`` or ``python
+matrix_optimizer_step_owned_amd/_build.py``); importing this package without it
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdmuon.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+DMUON_OK = 0
+DMUON_ERR_INVALID_ARG = -1
+DMUON_ERR_UNSUPPORTED = -2
+DMUON_ERR_WORKSPACE = -3
+DMUON_ERR_ALIASING = -4
+DMUON_ERR_HIP = -5
+
+DMUON_F32 = 0
+DMUON_BF16 = 1
+DMUON_NS_GRAM = 0
+DMUON_NS_DIRECT = 1
+DMUON_NS_PREC_BF16 = 0
+DMUON_NS_PREC_F32 = 1
+
+_BACKENDS = {"gram": DMUON_NS_GRAM, "direct": DMUON_NS_DIRECT}
+_PRECISIONS = {"bf16": DMUON_NS_PREC_BF16, "f32": DMUON_NS_PREC_F32}
+_DTYPES = {torch.float32: DMUON_F32, torch.bfloat16: DMUON_BF16}
+
+
+class dmuon_matrix_t(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("momentum", ctypes.c_void_p),
+                ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+
+
+class dmuon_hparams_t(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("momentum", ctypes.c_double),
+                ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+                ("weight_decay", ctypes.c_double),
+                ("ns_backend", ctypes.c_int32), ("ns_precision", ctypes.c_int32),
+                ("ns_coeffs", ctypes.POINTER(ctypes.c_double)),
+                ("ns_coeffs_len", ctypes.c_int32), ("eps", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_MP = ctypes.POINTER(dmuon_matrix_t)
+_HP = ctypes.POINTER(dmuon_hparams_t)
+
+EXPORTS = {
+    "dmuon_hparams_default": (None, [_HP]),
+    "dmuon_step_workspace_size": (ctypes.c_size_t, [_MP, ctypes.c_int32, _HP]),
+    "dmuon_step": (ctypes.c_int, [_MP, ctypes.c_int32, _HP, _P, ctypes.c_size_t, _P]),
+    "dmuon_momentum_workspace_size": (ctypes.c_size_t, [_MP, ctypes.c_int32]),
+    "dmuon_momentum": (ctypes.c_int, [_MP, ctypes.c_int32, _HP, _PP, ctypes.c_int32, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "dmuon_orthogonalize_workspace_size": (ctypes.c_size_t, [_I64P, _I64P, ctypes.c_int32, _HP]),
+    "dmuon_orthogonalize": (ctypes.c_int, [_PP, _PP, _I64P, _I64P, ctypes.c_int32, ctypes.c_int32,
+                                           _HP, _P, ctypes.c_size_t, _P]),
+    "dmuon_apply_update_workspace_size": (ctypes.c_size_t, [ctypes.c_int32]),
+    "dmuon_apply_update": (ctypes.c_int, [_MP, ctypes.c_int32, _PP, ctypes.c_int32, _HP, _P,
+                                          ctypes.c_size_t, _P]),
+    "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dmuon_last_error": (ctypes.c_char_p, []),
+    "dmuon_backend_info": (ctypes.c_char_p, []),
+    "dmuon_plan_describe": (ctypes.c_int64, [_I64P, _I64P, ctypes.c_int32, _HP, ctypes.c_char_p,
+                                             ctypes.c_size_t]),
+    "dmuon_profile_begin": (ctypes.c_int, []),
+    "dmuon_profile_end": (ctypes.c_int64, [ctypes.c_char_p, ctypes.c_size_t]),
+}
+
+for _name, (_res, _args) in EXPORTS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class DmuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _lib.dmuon_last_error().decode()
+        super().__init__(f"{where}: {_lib.dmuon_status_string(status).decode()} ({status}): {detail}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != DMUON_OK:
+        raise DmuonError(status, where)
+
+
+def dmuon_status_string(status: int) -> str:
+    return _lib.dmuon_status_string(status).decode()
+
+
+def dmuon_last_error() -> str:
+    return _lib.dmuon_last_error().decode()
+
+
+def dmuon_backend_info() -> dict:
+    return json.loads(_lib.dmuon_backend_info().decode())
+
+
+def dmuon_hparams_default() -> dict:
+    hp = dmuon_hparams_t()
+    _lib.dmuon_hparams_default(ctypes.byref(hp))
+    return dict(lr=hp.lr, momentum=hp.momentum, nesterov=bool(hp.nesterov), ns_steps=hp.ns_steps,
+                weight_decay=hp.weight_decay,
+                ns_backend={v: k for k, v in _BACKENDS.items()}[hp.ns_backend],
+                ns_precision={v: k for k, v in _PRECISIONS.items()}[hp.ns_precision],
+                ns_coeffs=None, eps=hp.eps)
+
+
+def _hparams(lr=0.02, momentum=0.95, nesterov=True, ns_steps=5, weight_decay=0.0,
+             ns_backend="gram", ns_precision="bf16", ns_coeffs=None, eps=1e-7):
+    hp = dmuon_hparams_t()
+    hp.lr = float(lr)
+    hp.momentum = float(momentum)
+    hp.nesterov = 1 if nesterov else 0
+    hp.ns_steps = int(ns_steps)
+    hp.weight_decay = float(weight_decay)
+    hp.ns_backend = _BACKENDS[ns_backend] if isinstance(ns_backend, str) else int(ns_backend)
+    hp.ns_precision = _PRECISIONS[ns_precision] if isinstance(ns_precision, str) else int(ns_precision)
+    keep = None
+    if ns_coeffs is not None:
+        flat = [float(v) for row in ns_coeffs for v in (row if hasattr(row, "__len__") else [row])]
+        keep = (ctypes.c_double * len(flat))(*flat)
+        hp.ns_coeffs = ctypes.cast(keep, ctypes.POINTER(ctypes.c_double))
+        hp.ns_coeffs_len = len(flat)
+    hp.eps = float(eps)
+    return hp, keep
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _mat(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _matrices(params, grads, momenta) -> ctypes.Array:
+    n = len(params)
+    arr = (dmuon_matrix_t * max(n, 1))()
+    for i in range(n):
+        p = _mat(params[i], f"params[{i}]")
+        m = arr[i]
+        m.rows, m.cols = p.shape
+        m.param = p.data_ptr()
+        m.param_dtype = _dtype(p)
+        g = grads[i] if grads is not None else None
+        if g is not None:
+            _mat(g, f"grads[{i}]")
+            if tuple(g.shape) != tuple(p.shape):
+                raise ValueError(f"grads[{i}] shape {tuple(g.shape)} != param shape {tuple(p.shape)}")
+            m.grad = g.data_ptr()
+            m.grad_dtype = _dtype(g)
+        else:
+            m.grad = None
+            m.grad_dtype = m.param_dtype
+        if momenta is not None and momenta[i] is not None:
+            b = _mat(momenta[i], f"momenta[{i}]")
+            if b.dtype != torch.float32 or tuple(b.shape) != tuple(p.shape):
+                raise ValueError(f"momenta[{i}] must be float32 of the param's shape")
+            m.momentum = b.data_ptr()
+        else:
+            m.momentum = None
+    return arr
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _ptrs(ts: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * max(len(ts), 1))()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr() if t is not None else None
+    return arr
+
+
+def dmuon_step_workspace_size(params, grads, momenta=None, **hp) -> int:
+    mats = _matrices(params, grads, momenta)
+    h, _k = _hparams(**hp)
+    return int(_lib.dmuon_step_workspace_size(mats, len(params), ctypes.byref(h)))
+
+
+def dmuon_step(params: List[torch.Tensor], grads: List[Optional[torch.Tensor]],
+               momenta: List[torch.Tensor], *, workspace: Optional[torch.Tensor] = None,
+               stream=None, **hp) -> None:
+    """One Muon step over a batch of owned matrices (in place on params and momenta)."""
+    n = len(params)
+    if n == 0:
+        return
+    mats = _matrices(params, grads, momenta)
+    h, _keep = _hparams(**hp)
+    nbytes = int(_lib.dmuon_step_workspace_size(mats, n, ctypes.byref(h)))
+    ws, wsb = _workspace(nbytes, params[0].device, workspace)
+    _check(_lib.dmuon_step(mats, n, ctypes.byref(h), ws.data_ptr() if ws is not None else None, wsb,
+                           _stream(stream, params[0].device)), "dmuon_step")
+
+
+def dmuon_momentum_workspace_size(grads, momenta) -> int:
+    mats = _matrices(momenta, grads, momenta)
+    return int(_lib.dmuon_momentum_workspace_size(mats, len(grads)))
+
+
+def dmuon_momentum(grads: List[torch.Tensor], momenta: List[torch.Tensor],
+                   ns_inputs: List[torch.Tensor], sumsq: torch.Tensor, *, momentum: float = 0.95,
+                   nesterov: bool = True, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    """Momentum stage: updates momenta, writes the wide-orientation NS inputs and sum(U^2)."""
+    n = len(grads)
+    if n == 0:
+        return
+    # the momentum buffers stand in for the (unused) params in the matrix records
+    mats = _matrices(momenta, grads, momenta)
+    dt = _dtype(ns_inputs[0])
+    for i, u in enumerate(ns_inputs):
+        r, c = grads[i].shape
+        if tuple(u.shape) != (min(r, c), max(r, c)) or _dtype(u) != dt or not u.is_contiguous():
+            raise ValueError(f"ns_inputs[{i}] must be a contiguous {min(r, c)}x{max(r, c)} tensor of one dtype")
+    if sumsq.dtype != torch.float64 or sumsq.numel() < n:
+        raise ValueError("sumsq must be a float64 tensor of n entries")
+    h, _keep = _hparams(momentum=momentum, nesterov=nesterov)
+    nbytes = int(_lib.dmuon_momentum_workspace_size(mats, n))
+    ws, wsb = _workspace(nbytes, grads[0].device, workspace)
+    _check(_lib.dmuon_momentum(mats, n, ctypes.byref(h), _ptrs(ns_inputs), dt, sumsq.data_ptr(),
+                               ws.data_ptr() if ws is not None else None, wsb,
+                               _stream(stream, grads[0].device)), "dmuon_momentum")
+
+
+def dmuon_orthogonalize_workspace_size(shapes: Sequence[Sequence[int]], **hp) -> int:
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    h, _k = _hparams(**hp)
+    return int(_lib.dmuon_orthogonalize_workspace_size(rows, cols, n, ctypes.byref(h)))
+
+
+def dmuon_orthogonalize(inputs: List[torch.Tensor], outputs: List[torch.Tensor], *,
+                        workspace: Optional[torch.Tensor] = None, stream=None, **hp) -> None:
+    """outputs[i] = NS(inputs[i]) (same shape and dtype as the input)."""
+    n = len(inputs)
+    if n == 0:
+        return
+    dt = _dtype(inputs[0])
+    for i in range(n):
+        _mat(inputs[i], f"inputs[{i}]")
+        _mat(outputs[i], f"outputs[{i}]")
+        if _dtype(inputs[i]) != dt or _dtype(outputs[i]) != dt or inputs[i].shape != outputs[i].shape:
+            raise ValueError(f"inputs[{i}] / outputs[{i}] must share one shape and dtype")
+    rows = (ctypes.c_int64 * n)(*[int(t.shape[0]) for t in inputs])
+    cols = (ctypes.c_int64 * n)(*[int(t.shape[1]) for t in inputs])
+    h, _keep = _hparams(**hp)
+    nbytes = int(_lib.dmuon_orthogonalize_workspace_size(rows, cols, n, ctypes.byref(h)))
+    ws, wsb = _workspace(nbytes, inputs[0].device, workspace)
+    _check(_lib.dmuon_orthogonalize(_ptrs(inputs), _ptrs(outputs), rows, cols, n, dt, ctypes.byref(h),
+                                    ws.data_ptr() if ws is not None else None, wsb,
+                                    _stream(stream, inputs[0].device)), "dmuon_orthogonalize")
+
+
+def dmuon_apply_update(params: List[torch.Tensor], updates: List[torch.Tensor], *, lr: float = 0.02,
+                       weight_decay: float = 0.0, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """W <- W*(1 - lr*wd) - lr*0.2*sqrt(max(m,n))*O for every matrix (in place)."""
+    n = len(params)
+    if n == 0:
+        return
+    mats = _matrices(params, None, None)
+    dt = _dtype(updates[0])
+    for i, u in enumerate(updates):
+        _mat(u, f"updates[{i}]")
+        if u.shape != params[i].shape or _dtype(u) != dt:
+            raise ValueError(f"updates[{i}] must have the param's shape and one dtype")
+    h, _keep = _hparams(lr=lr, weight_decay=weight_decay)
+    nbytes = int(_lib.dmuon_apply_update_workspace_size(n))
+    ws, wsb = _workspace(nbytes, params[0].device, workspace)
+    _check(_lib.dmuon_apply_update(mats, n, _ptrs(updates), dt, ctypes.byref(h),
+                                   ws.data_ptr() if ws is not None else None, wsb,
+                                   _stream(stream, params[0].device)), "dmuon_apply_update")
+
+
+def dmuon_plan_describe(shapes: Sequence[Sequence[int]], **hp) -> dict:
+    """The launch plan of these shapes (host only, no device needed)."""
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    h, _keep = _hparams(**hp)
+    need = _lib.dmuon_plan_describe(rows, cols, n, ctypes.byref(h), None, 0)
+    if need < 0:
+        raise DmuonError(int(need), "dmuon_plan_describe")
+    buf = ctypes.create_string_buffer(int(need) + 1)
+    _lib.dmuon_plan_describe(rows, cols, n, ctypes.byref(h), buf, int(need) + 1)
+    return json.loads(buf.value.decode())
+
+
+def dmuon_profile_begin() -> None:
+    """Start bracketing every library launch with HIP events."""
+    _check(_lib.dmuon_profile_begin(), "dmuon_profile_begin")
+
+
+def dmuon_profile_end() -> dict:
+    """Stop profiling; per kernel kind: launches, summed ms, algorithmic flops and bytes."""
+    need = _lib.dmuon_profile_end(None, 0)      # closes the window, keeps the report
+    if need < 0:
+        raise DmuonError(int(need), "dmuon_profile_end")
+    buf = ctypes.create_string_buffer(int(need) + 1)
+    _lib.dmuon_profile_end(buf, int(need) + 1)  # copies the kept report
+    return json.loads(buf.value.decode())

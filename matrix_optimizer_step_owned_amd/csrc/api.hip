@@ -1,0 +1,1143 @@
+// C-ABI entry points of the dmuon library: argument checks, the launch
+// planner (grouping every matrix's NS products into one launch per stage),
+// launch-table staging and the launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/dmuon.h"
+#include "internal.h"
+
+namespace dmuon {
+namespace {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+#define DMUON_HIP_TRY(expr)                                                              \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(DMUON_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));     \
+  } while (0)
+
+constexpr double kDefaultCoeffs[3] = {3.4445, -4.7750, 2.0315};
+constexpr int kMaxNsSteps = 16;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+size_t dtype_size(int32_t dt) { return dt == DT_F32 ? 4 : 2; }
+bool dtype_ok(int32_t dt) { return dt == DT_F32 || dt == DT_BF16; }
+
+// ---------------------------------------------------------------------------
+// hyperparameters
+// ---------------------------------------------------------------------------
+
+struct Coeffs {
+  std::vector<double> abc;  // 3 per step
+};
+
+int check_hparams(const dmuon_hparams_t* hp, bool need_momentum, Coeffs* out) {
+  if (!hp) return fail(DMUON_ERR_INVALID_ARG, "hparams is NULL");
+  if (hp->ns_steps < 0 || hp->ns_steps > kMaxNsSteps)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_steps must be in 0..16");
+  if (hp->ns_backend != DMUON_NS_GRAM && hp->ns_backend != DMUON_NS_DIRECT)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_backend must be DMUON_NS_GRAM or DMUON_NS_DIRECT");
+  if (hp->ns_precision != DMUON_NS_PREC_BF16 && hp->ns_precision != DMUON_NS_PREC_F32)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_precision must be BF16 or F32");
+  if (!std::isfinite(hp->eps) || hp->eps < 0) return fail(DMUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (need_momentum) {
+    if (!std::isfinite(hp->lr)) return fail(DMUON_ERR_INVALID_ARG, "lr must be finite");
+    if (!std::isfinite(hp->momentum)) return fail(DMUON_ERR_INVALID_ARG, "momentum must be finite");
+    if (!std::isfinite(hp->weight_decay)) return fail(DMUON_ERR_INVALID_ARG, "weight_decay must be finite");
+  }
+  const int K = hp->ns_steps;
+  out->abc.clear();
+  if (hp->ns_coeffs == nullptr) {
+    if (hp->ns_coeffs_len != 0) return fail(DMUON_ERR_INVALID_ARG, "ns_coeffs_len set but ns_coeffs is NULL");
+    for (int k = 0; k < K; ++k) out->abc.insert(out->abc.end(), kDefaultCoeffs, kDefaultCoeffs + 3);
+  } else if (hp->ns_coeffs_len == 3) {
+    for (int k = 0; k < K; ++k) out->abc.insert(out->abc.end(), hp->ns_coeffs, hp->ns_coeffs + 3);
+  } else if (hp->ns_coeffs_len == 3 * K && K > 0) {
+    out->abc.assign(hp->ns_coeffs, hp->ns_coeffs + 3 * K);
+  } else {
+    return fail(DMUON_ERR_INVALID_ARG, "ns_coeffs_len must be 3 or 3*ns_steps");
+  }
+  for (double v : out->abc)
+    if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "ns_coeffs must be finite");
+  return DMUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+enum Form : int32_t { FORM_DIRECT = 0, FORM_GRAM = 1 };
+
+// The Gram form pays off once the matrix is at least twice as wide as tall:
+// it replaces 15 m^2 n + 5 m^3 multiply-adds (symmetric tiles) by
+// 3 m^2 n + 17 m^3, and on near-square bf16 inputs its m x m iteration loses
+// accuracy, so squarer matrices keep the direct form.
+Form choose_form(int32_t backend, int64_t m, int64_t n) {
+  if (backend == DMUON_NS_DIRECT) return FORM_DIRECT;
+  return n >= 2 * m ? FORM_GRAM : FORM_DIRECT;
+}
+
+struct MatLayout {
+  int64_t rows, cols, m, n, mp, np;
+  bool tall;
+  Form form;
+  // byte offsets into the workspace (SIZE_MAX when unused)
+  size_t x0, x1, o, a, b, p, t, q0, q1;
+  size_t out;  // where O is left
+};
+
+// One GEMM as planned: pointers are workspace byte offsets.
+struct Op {
+  GemmKind kind;
+  int mat;
+  size_t A, B, C, Y;  // Y == SIZE_MAX: none
+  int64_t lda, ldb, ldc, ldy;
+  int32_t K, tiles_m, tiles_n, sym, alpha_pow, beta_pow, diag_limit;
+  float alpha, beta, gamma;
+  bool scaled;
+};
+
+struct Launch {
+  GemmKind kind;
+  int first;   // index into Plan::ops (sorted order)
+  int count;
+  int64_t tiles;
+  int64_t alg_flops;  // true-size flops, symmetric products counted once
+  int64_t alg_bytes;  // bytes an ideal kernel moves
+};
+
+struct Plan {
+  int n = 0;
+  int32_t prec = 0;
+  int ns_steps = 0;
+  int tile = 0;
+  std::vector<MatLayout> mats;
+  std::vector<Op> ops;            // grouped by launch
+  std::vector<Launch> launches;
+  std::vector<int64_t> blk_wide, blk_stored;
+  int64_t blocks_wide = 0, blocks_stored = 0;
+  // workspace layout
+  size_t off_ewmats = 0, off_tasks = 0, off_partials = 0, off_sumsq = 0, off_scale = 0;
+  size_t table_bytes = 0;   // EwMat[] + GemmTask[]
+  size_t ws_bytes = 0;
+};
+
+size_t kNone = SIZE_MAX;
+
+std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n, int32_t prec,
+                                 int32_t backend, const Coeffs& cf, bool with_ns) {
+  auto P = std::make_shared<Plan>();
+  P->n = n;
+  P->prec = prec;
+  P->ns_steps = with_ns ? static_cast<int>(cf.abc.size() / 3) : 0;
+  P->tile = prec == DMUON_NS_PREC_BF16 ? kTileBf16 : kTileF32;
+  const int64_t T = P->tile;
+  const size_t es = prec == DMUON_NS_PREC_BF16 ? 2 : 4;
+  const int K = P->ns_steps;
+
+  // table and scalars first
+  P->off_ewmats = 0;
+  size_t cur = align_up(sizeof(EwMat) * std::max(n, 1));
+  // GEMM ops are planned below; reserve their table space after counting.
+  P->blk_wide.resize(n);
+  P->blk_stored.resize(n);
+  P->mats.resize(n);
+  std::vector<std::vector<std::vector<Op>>> stages(n);
+  for (int i = 0; i < n; ++i) {
+    MatLayout& L = P->mats[i];
+    L.rows = rows[i];
+    L.cols = cols[i];
+    L.tall = rows[i] > cols[i];
+    L.m = std::min(rows[i], cols[i]);
+    L.n = std::max(rows[i], cols[i]);
+    L.mp = with_ns ? round_up(L.m, T) : L.m;
+    L.np = with_ns ? round_up(L.n, T) : L.n;
+    L.form = choose_form(backend, L.m, L.n);
+    L.x0 = L.x1 = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = kNone;
+    P->blk_wide[i] = P->blocks_wide;
+    P->blocks_wide += ((L.mp + kEwTile - 1) / kEwTile) * ((L.np + kEwTile - 1) / kEwTile);
+    P->blk_stored[i] = P->blocks_stored;
+    P->blocks_stored += ((L.rows + kEwTile - 1) / kEwTile) * ((L.cols + kEwTile - 1) / kEwTile);
+  }
+  return P;  // buffers are laid out by layout_plan()
+}
+
+// Per-matrix stage lists of the NS iteration.
+void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>>>& stages) {
+  const int K = P.ns_steps;
+  const int64_t T = P.tile;
+  stages.assign(P.n, {});
+  for (int i = 0; i < P.n; ++i) {
+    MatLayout& L = P.mats[i];
+    auto& st = stages[i];
+    if (K == 0) { L.out = L.x0; continue; }
+    const int32_t tm_mm = static_cast<int32_t>(L.mp / T);
+    const int32_t tn_mn = static_cast<int32_t>(L.np / T);
+    auto sym_op = [&](size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int32_t Kdim) {
+      Op o{};
+      o.kind = GemmKind::NT; o.mat = i;
+      o.A = A; o.B = B; o.C = C; o.Y = Y;
+      o.lda = o.ldb = ldab; o.ldc = L.mp; o.ldy = L.mp;
+      o.K = Kdim; o.tiles_m = o.tiles_n = tm_mm; o.sym = 1;
+      o.alpha = 1.f; o.beta = 0.f; o.gamma = 0.f; o.diag_limit = 0;
+      o.alpha_pow = o.beta_pow = 0; o.scaled = false;
+      return o;
+    };
+    if (L.form == FORM_DIRECT) {
+      for (int k = 0; k < K; ++k) {
+        const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
+        const size_t xin = (k % 2 == 0) ? L.x0 : L.x1;
+        const size_t xout = (k % 2 == 0) ? L.x1 : L.x0;
+        // A = s^2 X X^T (s folded in on the first step only)
+        Op g = sym_op(xin, xin, L.a, kNone, L.np, static_cast<int32_t>(L.np));
+        if (k == 0) { g.alpha_pow = 2; g.scaled = true; }
+        st.push_back({g});
+        // B = b A + c A A
+        Op h = sym_op(L.a, L.a, L.b, L.a, L.mp, static_cast<int32_t>(L.mp));
+        h.alpha = static_cast<float>(c);
+        h.beta = static_cast<float>(b);
+        st.push_back({h});
+        // X' = a X + B X
+        Op u{};
+        u.kind = GemmKind::NN; u.mat = i;
+        u.A = L.b; u.B = xin; u.C = xout; u.Y = xin;
+        u.lda = L.mp; u.ldb = L.np; u.ldc = L.np; u.ldy = L.np;
+        u.K = static_cast<int32_t>(L.mp); u.tiles_m = tm_mm; u.tiles_n = tn_mn; u.sym = 0;
+        u.alpha = 1.f; u.beta = static_cast<float>(a); u.gamma = 0.f; u.diag_limit = 0;
+        u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0; u.scaled = (k == 0);
+        st.push_back({u});
+      }
+      L.out = (K % 2 == 0) ? L.x0 : L.x1;
+    } else {
+      // R = s^2 X0 X0^T, kept in A
+      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.np, static_cast<int32_t>(L.np));
+      r.alpha_pow = 2; r.scaled = true;
+      st.push_back({r});
+      const size_t qbuf[2] = {L.q0, L.q1};
+      for (int k = 0; k < K; ++k) {
+        const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
+        const size_t pk = (k == 0) ? L.q0 : L.p;   // P_0 is Q itself
+        Op pp = sym_op(L.a, L.a, pk, L.a, L.mp, static_cast<int32_t>(L.mp));
+        pp.alpha = static_cast<float>(c);
+        pp.beta = static_cast<float>(b);
+        pp.gamma = static_cast<float>(a);
+        pp.diag_limit = static_cast<int32_t>(L.m);
+        st.push_back({pp});
+        std::vector<Op> next;
+        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.mp,
+                                          static_cast<int32_t>(L.mp)));          // Q <- P Q
+        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.mp,
+                                             static_cast<int32_t>(L.mp)));       // T = P A
+        if (!next.empty()) st.push_back(next);
+        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.mp,
+                                            static_cast<int32_t>(L.mp))});      // A = T P
+      }
+      Op f{};
+      f.kind = GemmKind::NN; f.mat = i;
+      f.A = qbuf[(K - 1) % 2]; f.B = L.x0; f.C = L.o; f.Y = kNone;
+      f.lda = L.mp; f.ldb = L.np; f.ldc = L.np; f.ldy = L.np;
+      f.K = static_cast<int32_t>(L.mp); f.tiles_m = tm_mm; f.tiles_n = tn_mn; f.sym = 0;
+      f.alpha = 1.f; f.beta = 0.f; f.gamma = 0.f; f.diag_limit = 0;
+      f.alpha_pow = 1; f.beta_pow = 0; f.scaled = true;
+      st.push_back({f});
+      L.out = L.o;
+    }
+  }
+}
+
+int64_t op_tiles(const Op& o) {
+  return o.sym ? int64_t(o.tiles_m) * (o.tiles_m + 1) / 2 : int64_t(o.tiles_m) * o.tiles_n;
+}
+
+// Lay out workspace buffers and group ops into launches.
+void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
+  const size_t es = P.prec == DMUON_NS_PREC_BF16 ? 2 : 4;
+  // buffers
+  size_t cur = 0;  // relative to the start of the matrix region
+  for (auto& L : P.mats) {
+    const size_t mn = align_up(size_t(L.mp) * L.np * es);
+    const size_t mm = align_up(size_t(L.mp) * L.mp * es);
+    L.x0 = cur; cur += mn;
+    if (!with_ns || P.ns_steps == 0) continue;
+    if (L.form == FORM_DIRECT) {
+      L.x1 = cur; cur += mn;
+      L.a = cur; cur += mm;
+      L.b = cur; cur += mm;
+    } else {
+      L.o = cur; cur += mn;
+      L.a = cur; cur += mm;
+      L.p = cur; cur += mm;
+      L.t = cur; cur += mm;
+      L.q0 = cur; cur += mm;
+      L.q1 = cur; cur += mm;
+    }
+  }
+  const size_t mat_region = cur;
+
+  std::vector<std::vector<std::vector<Op>>> stages;
+  if (with_ns) plan_ops(P, cf, stages);
+  else for (auto& L : P.mats) L.out = L.x0;
+
+  // group: stage s, NT then NN; largest K first (LPT order)
+  size_t max_st = 0;
+  for (auto& st : stages) max_st = std::max(max_st, st.size());
+  P.ops.clear();
+  P.launches.clear();
+  for (size_t s = 0; s < max_st; ++s) {
+    for (GemmKind kind : {GemmKind::NT, GemmKind::NN}) {
+      std::vector<Op> group;
+      for (auto& st : stages)
+        if (s < st.size())
+          for (auto& o : st[s])
+            if (o.kind == kind) group.push_back(o);
+      if (group.empty()) continue;
+      std::stable_sort(group.begin(), group.end(), [](const Op& x, const Op& y) { return x.K > y.K; });
+      Launch l{kind, static_cast<int>(P.ops.size()), static_cast<int>(group.size()), 0, 0, 0};
+      const int64_t es = P.prec == DMUON_NS_PREC_BF16 ? 2 : 4;
+      for (auto& o : group) {
+        l.tiles += op_tiles(o);
+        const MatLayout& L = P.mats[o.mat];
+        const int64_t m = L.m, n = L.n;
+        const bool has_y = o.Y != kNone;
+        if (o.kind == GemmKind::NT) {
+          const int64_t kr = (o.K == L.np) ? n : m;   // X X^T reads m x n, others m x m
+          l.alg_flops += m * (m + 1) * kr;
+          l.alg_bytes += es * (m * kr * (o.A == o.B ? 1 : 2) + (has_y ? m * m : 0) + m * m);
+        } else {
+          l.alg_flops += 2 * m * n * m;
+          l.alg_bytes += es * (m * m + m * n + (has_y ? m * n : 0) + m * n);
+        }
+      }
+      P.ops.insert(P.ops.end(), group.begin(), group.end());
+      P.launches.push_back(l);
+    }
+  }
+
+  // workspace: [EwMat table][GemmTask table][partials][sumsq][scale][matrices]
+  size_t off = 0;
+  P.off_ewmats = off;
+  off += align_up(sizeof(EwMat) * std::max(P.n, 1));
+  P.off_tasks = off;
+  off += align_up(sizeof(GemmTask) * std::max<size_t>(P.ops.size(), 1));
+  P.table_bytes = off;
+  P.off_partials = off;
+  off += align_up(sizeof(float) * std::max<int64_t>(P.blocks_wide, 1));
+  P.off_sumsq = off;
+  off += align_up(sizeof(double) * std::max(P.n, 1));
+  P.off_scale = off;
+  off += align_up(sizeof(float) * std::max(P.n, 1));
+  for (auto& L : P.mats) {
+    for (size_t* f : {&L.x0, &L.x1, &L.o, &L.a, &L.b, &L.p, &L.t, &L.q0, &L.q1, &L.out})
+      if (*f != kNone) *f += off;
+  }
+  for (auto& o : P.ops)
+    for (size_t* f : {&o.A, &o.B, &o.C, &o.Y})
+      if (*f != kNone) *f += off;
+  P.ws_bytes = off + mat_region;
+}
+
+// ---------------------------------------------------------------------------
+// plan cache
+// ---------------------------------------------------------------------------
+
+std::mutex g_plan_mu;
+std::unordered_map<std::string, std::shared_ptr<Plan>> g_plans;
+
+std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
+                               int32_t prec, int32_t backend, const Coeffs& cf, bool with_ns) {
+  std::string key;
+  key.reserve(32 + rows.size() * 16 + cf.abc.size() * 8);
+  auto put = [&](const void* p, size_t n) { key.append(static_cast<const char*>(p), n); };
+  const int32_t hdr[3] = {prec, with_ns ? backend : -1, with_ns ? 1 : 0};
+  put(hdr, sizeof(hdr));
+  const int64_t n = static_cast<int64_t>(rows.size());
+  put(&n, sizeof(n));
+  put(rows.data(), rows.size() * sizeof(int64_t));
+  put(cols.data(), cols.size() * sizeof(int64_t));
+  if (with_ns) put(cf.abc.data(), cf.abc.size() * sizeof(double));
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) return it->second;
+  }
+  auto P = build_plan(rows.data(), cols.data(), static_cast<int>(rows.size()), prec, backend, cf, with_ns);
+  layout_plan(*P, cf, with_ns);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (g_plans.size() > 256) g_plans.clear();
+  g_plans.emplace(key, P);
+  return P;
+}
+
+// ---------------------------------------------------------------------------
+// device check and launch-table staging
+// ---------------------------------------------------------------------------
+
+struct DeviceState {
+  bool checked = false;
+  bool ok = false;
+  std::string arch;
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  Slot slots[4];
+  int next = 0;
+};
+
+std::mutex g_dev_mu;
+std::map<int, DeviceState> g_dev;
+
+int current_device_state(DeviceState** out) {
+  int dev = 0;
+  DMUON_HIP_TRY(hipGetDevice(&dev));
+  DeviceState& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    DMUON_HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    d.arch = prop.gcnArchName;
+    d.ok = d.arch.rfind("gfx950", 0) == 0;
+    d.checked = true;
+  }
+  if (!d.ok) return fail(DMUON_ERR_UNSUPPORTED, "device arch " + d.arch + " is not gfx950");
+  *out = &d;
+  return DMUON_OK;
+}
+
+// Copy `bytes` of launch table, built by `fill` into pinned host memory, to
+// device address `dst` on `stream`.  A ring of four pinned buffers, each
+// guarded by an event, lets the host run ahead of the device.
+template <class Fill>
+int stage_table(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceState* d = nullptr;
+  int st = current_device_state(&d);
+  if (st != DMUON_OK) return st;
+  DeviceState::Slot& s = d->slots[d->next];
+  d->next = (d->next + 1) % 4;
+  if (s.pending) {
+    DMUON_HIP_TRY(hipEventSynchronize(s.ev));
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host) DMUON_HIP_TRY(hipHostFree(s.host));
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
+    DMUON_HIP_TRY(hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    s.cap = cap;
+  }
+  if (!s.ev) DMUON_HIP_TRY(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  std::memset(s.host, 0, bytes);
+  fill(static_cast<char*>(s.host));
+  DMUON_HIP_TRY(hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream));
+  DMUON_HIP_TRY(hipEventRecord(s.ev, stream));
+  s.pending = true;
+  return DMUON_OK;
+}
+
+int check_device() {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceState* d = nullptr;
+  return current_device_state(&d);
+}
+
+// ---------------------------------------------------------------------------
+// measurement hooks
+// ---------------------------------------------------------------------------
+
+enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_NT_BF16, PK_GEMM_NN_BF16, PK_GEMM_NT_F32,
+                PK_GEMM_NN_F32, PK_UPDATE, PK_COUNT };
+const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_nt_bf16", "gemm_nn_bf16",
+                                          "gemm_nt_f32", "gemm_nn_f32", "update"};
+
+struct ProfRec {
+  int kind;
+  int64_t flops, bytes;
+  hipEvent_t a, b;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+template <class F>
+hipError_t prof_launch(int kind, int64_t flops, int64_t bytes, hipStream_t stream, F launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return launch();
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  if (e == hipSuccess) e = hipEventRecord(a, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, stream);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof.push_back({kind, flops, bytes, a, b});
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// validation helpers
+// ---------------------------------------------------------------------------
+
+struct Range {
+  uintptr_t lo, hi;
+  std::string what;
+};
+
+int check_overlaps(std::vector<Range>& r) {
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].lo < r[i - 1].hi)
+      return fail(DMUON_ERR_ALIASING, r[i - 1].what + " overlaps " + r[i].what);
+  return DMUON_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+float lr_eff_of(double lr, int64_t rows, int64_t cols) {
+  return static_cast<float>(lr * 0.2 * std::sqrt(static_cast<double>(std::max(rows, cols))));
+}
+
+void fill_tasks(const Plan& P, char* ws_base, GemmTask* out) {
+  auto ptr = [&](size_t off) -> void* { return off == kNone ? nullptr : ws_base + off; };
+  int64_t first_tile = 0;
+  for (const Launch& l : P.launches) {
+    int64_t tile = 0;
+    for (int j = 0; j < l.count; ++j) {
+      const Op& o = P.ops[l.first + j];
+      GemmTask& t = out[l.first + j];
+      t.A = ptr(o.A);
+      t.B = ptr(o.B);
+      t.C = ptr(o.C);
+      t.Y = ptr(o.Y);
+      t.scale = o.scaled ? reinterpret_cast<const float*>(ws_base + P.off_scale) + o.mat : nullptr;
+      t.lda = o.lda; t.ldb = o.ldb; t.ldc = o.ldc; t.ldy = o.ldy;
+      t.K = o.K; t.tiles_m = o.tiles_m; t.tiles_n = o.tiles_n; t.sym = o.sym;
+      t.alpha_pow = o.alpha_pow; t.beta_pow = o.beta_pow; t.diag_limit = o.diag_limit;
+      t.tile_begin = static_cast<int32_t>(tile);
+      t.alpha = o.alpha; t.beta = o.beta; t.gamma = o.gamma;
+      tile += op_tiles(o);
+    }
+    (void)first_tile;
+  }
+}
+
+int run_gemms(const Plan& P, char* ws, hipStream_t stream) {
+  const GemmTask* tasks = reinterpret_cast<const GemmTask*>(ws + P.off_tasks);
+  for (const Launch& l : P.launches) {
+    const bool bf = P.prec == DMUON_NS_PREC_BF16;
+    const int kind = bf ? (l.kind == GemmKind::NT ? PK_GEMM_NT_BF16 : PK_GEMM_NN_BF16)
+                        : (l.kind == GemmKind::NT ? PK_GEMM_NT_F32 : PK_GEMM_NN_F32);
+    hipError_t e = prof_launch(kind, l.alg_flops, l.alg_bytes, stream, [&] {
+      return bf ? launch_gemm_bf16(l.kind, tasks + l.first, l.count, l.tiles, P.tile, stream)
+                : launch_gemm_f32(l.kind, tasks + l.first, l.count, l.tiles, P.tile, stream);
+    });
+    if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("GEMM launch: ") + hipGetErrorString(e));
+  }
+  return DMUON_OK;
+}
+
+int check_matrix_fields(const dmuon_matrix_t& m, int i, bool need_grad_mom) {
+  char buf[160];
+  if (m.rows <= 0 || m.cols <= 0) {
+    std::snprintf(buf, sizeof buf, "matrix %d: rows and cols must be > 0", i);
+    return fail(DMUON_ERR_INVALID_ARG, buf);
+  }
+  if (m.rows > (1LL << 30) || m.cols > (1LL << 30)) {
+    std::snprintf(buf, sizeof buf, "matrix %d: dimension above 2^30", i);
+    return fail(DMUON_ERR_INVALID_ARG, buf);
+  }
+  if (!dtype_ok(m.param_dtype) || !dtype_ok(m.grad_dtype)) {
+    std::snprintf(buf, sizeof buf, "matrix %d: dtype must be DMUON_F32 or DMUON_BF16", i);
+    return fail(DMUON_ERR_UNSUPPORTED, buf);
+  }
+  if (need_grad_mom && m.momentum == nullptr) {
+    std::snprintf(buf, sizeof buf, "matrix %d: momentum is NULL", i);
+    return fail(DMUON_ERR_INVALID_ARG, buf);
+  }
+  return DMUON_OK;
+}
+
+std::string mat_name(const char* what, int i) { return std::string(what) + "[" + std::to_string(i) + "]"; }
+
+}  // namespace
+}  // namespace dmuon
+
+using namespace dmuon;
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+void dmuon_hparams_default(dmuon_hparams_t* hp) {
+  if (!hp) return;
+  hp->lr = 0.02;
+  hp->momentum = 0.95;
+  hp->nesterov = 1;
+  hp->ns_steps = 5;
+  hp->weight_decay = 0.0;
+  hp->ns_backend = DMUON_NS_GRAM;
+  hp->ns_precision = DMUON_NS_PREC_BF16;
+  hp->ns_coeffs = nullptr;
+  hp->ns_coeffs_len = 0;
+  hp->eps = 1e-7;
+}
+
+const char* dmuon_status_string(int status) {
+  switch (status) {
+    case DMUON_OK: return "ok";
+    case DMUON_ERR_INVALID_ARG: return "invalid argument";
+    case DMUON_ERR_UNSUPPORTED: return "unsupported dtype or device";
+    case DMUON_ERR_WORKSPACE: return "workspace missing or too small";
+    case DMUON_ERR_ALIASING: return "buffers overlap";
+    case DMUON_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dmuon_last_error(void) { return g_last_error.c_str(); }
+
+const char* dmuon_backend_info(void) {
+  return "{\"arch\": \"gfx950\", "
+         "\"ns_gemm_bf16\": \"grouped 128x128x64 tiles, 4 waves of 64x64, "
+         "v_mfma_f32_32x32x16_bf16, fp32 accumulate, swizzled LDS double buffer; "
+         "NT symmetric (upper-triangle tiles, mirrored store) and NN (register-transposed B)\", "
+         "\"ns_gemm_f32\": \"grouped 64x64x16 tiles, v_mfma_f32_32x32x2f32\", "
+         "\"elementwise\": \"64x64 tiles, 256 threads, LDS transpose for tall matrices, "
+         "wave-shuffle sum of squares with fp64 per-matrix finish\", "
+         "\"gram_rule\": \"ns_backend gram uses the Gram form when max(m,n) >= 2*min(m,n), "
+         "the direct form otherwise\"}";
+}
+
+// ---- dmuon_step ------------------------------------------------------------
+
+static int step_prepare(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                        Coeffs* cf, std::vector<int>* active, std::shared_ptr<Plan>* plan) {
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !mats) return fail(DMUON_ERR_INVALID_ARG, "mats is NULL");
+  int st = check_hparams(hp, true, cf);
+  if (st) return st;
+  std::vector<int64_t> rows, cols;
+  for (int i = 0; i < n; ++i) {
+    st = check_matrix_fields(mats[i], i, true);
+    if (st) return st;
+    if (!mats[i].param) return fail(DMUON_ERR_INVALID_ARG, mat_name("param", i) + " is NULL");
+    if (!mats[i].grad) continue;
+    active->push_back(i);
+    rows.push_back(mats[i].rows);
+    cols.push_back(mats[i].cols);
+  }
+  *plan = get_plan(rows, cols, hp->ns_precision, hp->ns_backend, *cf, true);
+  return DMUON_OK;
+}
+
+size_t dmuon_step_workspace_size(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp) {
+  Coeffs cf;
+  std::vector<int> active;
+  std::shared_ptr<Plan> plan;
+  if (step_prepare(mats, n, hp, &cf, &active, &plan) != DMUON_OK) return 0;
+  return active.empty() ? 0 : plan->ws_bytes;
+}
+
+int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp, void* workspace,
+               size_t workspace_bytes, void* stream_) {
+  g_last_error.clear();
+  Coeffs cf;
+  std::vector<int> active;
+  std::shared_ptr<Plan> plan;
+  int st = step_prepare(mats, n, hp, &cf, &active, &plan);
+  if (st) return st;
+  if (active.empty()) return DMUON_OK;
+  const Plan& P = *plan;
+  if (!workspace || workspace_bytes < P.ws_bytes) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "workspace needs %zu bytes, got %zu", P.ws_bytes, workspace_bytes);
+    return fail(DMUON_ERR_WORKSPACE, buf);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::vector<Range> ranges;
+  for (int i : active) {
+    const dmuon_matrix_t& m = mats[i];
+    const size_t ne = size_t(m.rows) * m.cols;
+    auto add = [&](const void* p, size_t bytes, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      ranges.push_back({lo, lo + bytes, mat_name(what, i)});
+    };
+    add(m.param, ne * dtype_size(m.param_dtype), "param");
+    add(m.grad, ne * dtype_size(m.grad_dtype), "grad");
+    add(m.momentum, ne * 4, "momentum");
+  }
+  ranges.push_back({reinterpret_cast<uintptr_t>(workspace),
+                    reinterpret_cast<uintptr_t>(workspace) + P.ws_bytes, "workspace"});
+  st = check_overlaps(ranges);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
+  const float decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+    EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
+    for (int j = 0; j < P.n; ++j) {
+      const dmuon_matrix_t& m = mats[active[j]];
+      const MatLayout& L = P.mats[j];
+      EwMat& e = em[j];
+      e.rows = m.rows; e.cols = m.cols;
+      e.src = m.grad; e.mom = m.momentum; e.param = m.param;
+      e.u_dst = ws + L.x0; e.o_src = ws + L.out;
+      e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
+      e.tall = L.tall; e.src_dtype = m.grad_dtype; e.wide_dtype = wide_dt; e.param_dtype = m.param_dtype;
+      e.scale_idx = P.ns_steps == 0 ? j : -1;
+      e.aligned = (m.cols % 4 == 0) && aligned16(m.grad) && aligned16(m.momentum) && aligned16(m.param);
+      e.user_index = j;
+      e.blk_wide = P.blk_wide[j]; e.blk_stored = P.blk_stored[j];
+      e.lr_eff = lr_eff_of(hp->lr, m.rows, m.cols);
+      e.decay = decay;
+    }
+    fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks));
+  });
+  if (st) return st;
+  const EwMat* em_dev = reinterpret_cast<const EwMat*>(ws + P.off_ewmats);
+  float* partials = reinterpret_cast<float*>(ws + P.off_partials);
+  float* scale = reinterpret_cast<float*>(ws + P.off_scale);
+  double* sumsq = reinterpret_cast<double*>(ws + P.off_sumsq);
+  int64_t mom_bytes = 0, upd_bytes = 0;
+  for (int j = 0; j < P.n; ++j) {
+    const dmuon_matrix_t& m = mats[active[j]];
+    const int64_t ne = m.rows * m.cols;
+    mom_bytes += ne * (int64_t(dtype_size(m.grad_dtype)) + 8 + int64_t(dtype_size(wide_dt)));
+    upd_bytes += ne * (2 * int64_t(dtype_size(m.param_dtype)) + int64_t(dtype_size(wide_dt)));
+  }
+  DMUON_HIP_TRY(prof_launch(PK_MOMENTUM, 0, mom_bytes, stream, [&] {
+    return launch_momentum(em_dev, P.n, P.blocks_wide, 0, static_cast<float>(hp->momentum),
+                           hp->nesterov ? 1 : 0, partials, stream);
+  }));
+  DMUON_HIP_TRY(prof_launch(PK_FINALIZE, 0, P.blocks_wide * 4, stream, [&] {
+    return launch_finalize(em_dev, P.n, P.blocks_wide, partials, sumsq, scale, hp->eps, stream);
+  }));
+  st = run_gemms(P, ws, stream);
+  if (st) return st;
+  DMUON_HIP_TRY(prof_launch(PK_UPDATE, 0, upd_bytes, stream, [&] {
+    return launch_update(em_dev, P.n, P.blocks_stored, 0, scale, stream);
+  }));
+  return DMUON_OK;
+}
+
+// ---- dmuon_momentum --------------------------------------------------------
+
+size_t dmuon_momentum_workspace_size(const dmuon_matrix_t* mats, int32_t n) {
+  if (n <= 0 || !mats) return 0;
+  std::vector<int64_t> rows, cols;
+  for (int i = 0; i < n; ++i)
+    if (mats[i].grad && mats[i].rows > 0 && mats[i].cols > 0) {
+      rows.push_back(mats[i].rows);
+      cols.push_back(mats[i].cols);
+    }
+  if (rows.empty()) return 0;
+  Coeffs cf;
+  auto P = get_plan(rows, cols, DMUON_NS_PREC_F32, 0, cf, false);
+  return P->off_sumsq;  // tables and partials only
+}
+
+int dmuon_momentum(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                   void* const* ns_input, int32_t ns_input_dtype, double* sumsq, void* workspace,
+                   size_t workspace_bytes, void* stream_) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && (!mats || !ns_input || !sumsq)) return fail(DMUON_ERR_INVALID_ARG, "mats, ns_input or sumsq is NULL");
+  if (!hp) return fail(DMUON_ERR_INVALID_ARG, "hparams is NULL");
+  if (!std::isfinite(hp->momentum)) return fail(DMUON_ERR_INVALID_ARG, "momentum must be finite");
+  if (!dtype_ok(ns_input_dtype)) return fail(DMUON_ERR_UNSUPPORTED, "ns_input_dtype must be F32 or BF16");
+  std::vector<int> active;
+  std::vector<int64_t> rows, cols;
+  for (int i = 0; i < n; ++i) {
+    int st = check_matrix_fields(mats[i], i, true);
+    if (st) return st;
+    if (!mats[i].grad) continue;
+    if (!ns_input[i]) return fail(DMUON_ERR_INVALID_ARG, mat_name("ns_input", i) + " is NULL");
+    active.push_back(i);
+    rows.push_back(mats[i].rows);
+    cols.push_back(mats[i].cols);
+  }
+  if (active.empty()) return DMUON_OK;
+  Coeffs cf;
+  auto plan = get_plan(rows, cols, DMUON_NS_PREC_F32, 0, cf, false);
+  const Plan& P = *plan;
+  const size_t need = P.off_sumsq;
+  if (!workspace || workspace_bytes < need) return fail(DMUON_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::vector<Range> ranges;
+  for (int i : active) {
+    const dmuon_matrix_t& m = mats[i];
+    const size_t ne = size_t(m.rows) * m.cols;
+    auto add = [&](const void* p, size_t bytes, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      ranges.push_back({lo, lo + bytes, mat_name(what, i)});
+    };
+    add(m.grad, ne * dtype_size(m.grad_dtype), "grad");
+    add(m.momentum, ne * 4, "momentum");
+    add(ns_input[i], ne * dtype_size(ns_input_dtype), "ns_input");
+  }
+  ranges.push_back({reinterpret_cast<uintptr_t>(sumsq), reinterpret_cast<uintptr_t>(sumsq) + 8 * size_t(n), "sumsq"});
+  ranges.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need, "workspace"});
+  int st = check_overlaps(ranges);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  st = stage_table(ws, P.off_ewmats + sizeof(EwMat) * P.n, stream, [&](char* host) {
+    EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
+    for (int j = 0; j < P.n; ++j) {
+      const dmuon_matrix_t& m = mats[active[j]];
+      const MatLayout& L = P.mats[j];
+      EwMat& e = em[j];
+      e.rows = m.rows; e.cols = m.cols;
+      e.src = m.grad; e.mom = m.momentum; e.param = nullptr;
+      e.u_dst = ns_input[active[j]]; e.o_src = nullptr;
+      e.ld_wide = L.n; e.wide_rows = static_cast<int32_t>(L.m); e.wide_cols = static_cast<int32_t>(L.n);
+      e.tall = L.tall; e.src_dtype = m.grad_dtype; e.wide_dtype = ns_input_dtype; e.param_dtype = m.param_dtype;
+      e.scale_idx = -1;
+      e.aligned = (m.cols % 4 == 0) && aligned16(m.grad) && aligned16(m.momentum);
+      e.user_index = active[j];
+      e.blk_wide = P.blk_wide[j]; e.blk_stored = P.blk_stored[j];
+      e.lr_eff = 0.f; e.decay = 1.f;
+    }
+  });
+  if (st) return st;
+  const EwMat* em_dev = reinterpret_cast<const EwMat*>(ws + P.off_ewmats);
+  float* partials = reinterpret_cast<float*>(ws + P.off_partials);
+  DMUON_HIP_TRY(launch_momentum(em_dev, P.n, P.blocks_wide, 0, static_cast<float>(hp->momentum),
+                                hp->nesterov ? 1 : 0, partials, stream));
+  DMUON_HIP_TRY(launch_finalize(em_dev, P.n, P.blocks_wide, partials, sumsq, nullptr, 0.0, stream));
+  return DMUON_OK;
+}
+
+// ---- dmuon_orthogonalize -----------------------------------------------------
+
+static int ortho_prepare(const int64_t* rows, const int64_t* cols, int32_t n, const dmuon_hparams_t* hp,
+                         Coeffs* cf, std::shared_ptr<Plan>* plan) {
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && (!rows || !cols)) return fail(DMUON_ERR_INVALID_ARG, "rows or cols is NULL");
+  int st = check_hparams(hp, false, cf);
+  if (st) return st;
+  for (int i = 0; i < n; ++i)
+    if (rows[i] <= 0 || cols[i] <= 0 || rows[i] > (1LL << 30) || cols[i] > (1LL << 30))
+      return fail(DMUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": bad shape");
+  if (n == 0) return DMUON_OK;
+  *plan = get_plan(std::vector<int64_t>(rows, rows + n), std::vector<int64_t>(cols, cols + n),
+                   hp->ns_precision, hp->ns_backend, *cf, true);
+  return DMUON_OK;
+}
+
+size_t dmuon_orthogonalize_workspace_size(const int64_t* rows, const int64_t* cols, int32_t n,
+                                          const dmuon_hparams_t* hp) {
+  Coeffs cf;
+  std::shared_ptr<Plan> plan;
+  if (ortho_prepare(rows, cols, n, hp, &cf, &plan) != DMUON_OK || n == 0) return 0;
+  return plan->ws_bytes;
+}
+
+int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* rows, const int64_t* cols,
+                        int32_t n, int32_t io_dtype, const dmuon_hparams_t* hp, void* workspace,
+                        size_t workspace_bytes, void* stream_) {
+  g_last_error.clear();
+  Coeffs cf;
+  std::shared_ptr<Plan> plan;
+  int st = ortho_prepare(rows, cols, n, hp, &cf, &plan);
+  if (st) return st;
+  if (n == 0) return DMUON_OK;
+  if (!in || !out) return fail(DMUON_ERR_INVALID_ARG, "in or out is NULL");
+  if (!dtype_ok(io_dtype)) return fail(DMUON_ERR_UNSUPPORTED, "io_dtype must be F32 or BF16");
+  const Plan& P = *plan;
+  if (!workspace || workspace_bytes < P.ws_bytes) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "workspace needs %zu bytes, got %zu", P.ws_bytes, workspace_bytes);
+    return fail(DMUON_ERR_WORKSPACE, buf);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::vector<Range> outs, ins;
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
+  for (int i = 0; i < n; ++i) {
+    if (!in[i] || !out[i]) return fail(DMUON_ERR_INVALID_ARG, "in[" + std::to_string(i) + "] or out is NULL");
+    const size_t bytes = size_t(rows[i]) * cols[i] * dtype_size(io_dtype);
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out[i]), s = reinterpret_cast<uintptr_t>(in[i]);
+    outs.push_back({o, o + bytes, mat_name("out", i)});
+    ins.push_back({s, s + bytes, mat_name("in", i)});
+  }
+  {
+    std::vector<Range> r = outs;
+    r.push_back({wlo, wlo + P.ws_bytes, "workspace"});
+    st = check_overlaps(r);
+    if (st) return st;
+    for (int i = 0; i < n; ++i) {
+      if (ins[i].lo < wlo + P.ws_bytes && wlo < ins[i].hi) return fail(DMUON_ERR_ALIASING, ins[i].what + " overlaps workspace");
+      for (int j = 0; j < n; ++j) {
+        if (i == j) {
+          if (ins[i].lo != outs[i].lo && ins[i].lo < outs[i].hi && outs[i].lo < ins[i].hi)
+            return fail(DMUON_ERR_ALIASING, ins[i].what + " partially overlaps " + outs[i].what);
+        } else if (ins[i].lo < outs[j].hi && outs[j].lo < ins[i].hi) {
+          return fail(DMUON_ERR_ALIASING, ins[i].what + " overlaps " + outs[j].what);
+        }
+      }
+    }
+  }
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
+  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+    EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
+    for (int j = 0; j < P.n; ++j) {
+      const MatLayout& L = P.mats[j];
+      EwMat& e = em[j];
+      e.rows = rows[j]; e.cols = cols[j];
+      e.src = in[j]; e.mom = nullptr; e.param = out[j];
+      e.u_dst = ws + L.x0; e.o_src = ws + L.out;
+      e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
+      e.tall = L.tall; e.src_dtype = io_dtype; e.wide_dtype = wide_dt; e.param_dtype = io_dtype;
+      e.scale_idx = P.ns_steps == 0 ? j : -1;
+      e.aligned = (cols[j] % 4 == 0) && aligned16(in[j]) && aligned16(out[j]);
+      e.user_index = j;
+      e.blk_wide = P.blk_wide[j]; e.blk_stored = P.blk_stored[j];
+      e.lr_eff = 0.f; e.decay = 1.f;
+    }
+    fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks));
+  });
+  if (st) return st;
+  const EwMat* em_dev = reinterpret_cast<const EwMat*>(ws + P.off_ewmats);
+  float* partials = reinterpret_cast<float*>(ws + P.off_partials);
+  float* scale = reinterpret_cast<float*>(ws + P.off_scale);
+  double* sumsq = reinterpret_cast<double*>(ws + P.off_sumsq);
+  DMUON_HIP_TRY(launch_momentum(em_dev, P.n, P.blocks_wide, 1, 0.f, 0, partials, stream));
+  DMUON_HIP_TRY(launch_finalize(em_dev, P.n, P.blocks_wide, partials, sumsq, scale, hp->eps, stream));
+  st = run_gemms(P, ws, stream);
+  if (st) return st;
+  DMUON_HIP_TRY(launch_update(em_dev, P.n, P.blocks_stored, 1, scale, stream));
+  return DMUON_OK;
+}
+
+// ---- dmuon_apply_update -----------------------------------------------------
+
+size_t dmuon_apply_update_workspace_size(int32_t n) {
+  return n <= 0 ? 0 : align_up(sizeof(EwMat) * n);
+}
+
+int dmuon_apply_update(const dmuon_matrix_t* mats, int32_t n, const void* const* update, int32_t update_dtype,
+                       const dmuon_hparams_t* hp, void* workspace, size_t workspace_bytes, void* stream_) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return DMUON_OK;
+  if (!mats || !update) return fail(DMUON_ERR_INVALID_ARG, "mats or update is NULL");
+  if (!hp) return fail(DMUON_ERR_INVALID_ARG, "hparams is NULL");
+  if (!std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+    return fail(DMUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
+  if (!dtype_ok(update_dtype)) return fail(DMUON_ERR_UNSUPPORTED, "update_dtype must be F32 or BF16");
+  const size_t need = dmuon_apply_update_workspace_size(n);
+  if (!workspace || workspace_bytes < need) return fail(DMUON_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  std::vector<Range> ranges;
+  std::vector<int64_t> blk(n);
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const dmuon_matrix_t& m = mats[i];
+    int st = check_matrix_fields(m, i, false);
+    if (st) return st;
+    if (!m.param || !update[i]) return fail(DMUON_ERR_INVALID_ARG, mat_name("param/update", i) + " is NULL");
+    const size_t ne = size_t(m.rows) * m.cols;
+    const uintptr_t p = reinterpret_cast<uintptr_t>(m.param), u = reinterpret_cast<uintptr_t>(update[i]);
+    ranges.push_back({p, p + ne * dtype_size(m.param_dtype), mat_name("param", i)});
+    ranges.push_back({u, u + ne * dtype_size(update_dtype), mat_name("update", i)});
+    blk[i] = blocks;
+    blocks += ((m.rows + kEwTile - 1) / kEwTile) * ((m.cols + kEwTile - 1) / kEwTile);
+  }
+  ranges.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need, "workspace"});
+  int st = check_overlaps(ranges);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const float decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+  st = stage_table(ws, sizeof(EwMat) * n, stream, [&](char* host) {
+    EwMat* em = reinterpret_cast<EwMat*>(host);
+    for (int j = 0; j < n; ++j) {
+      const dmuon_matrix_t& m = mats[j];
+      EwMat& e = em[j];
+      e.rows = m.rows; e.cols = m.cols;
+      e.src = nullptr; e.mom = nullptr; e.param = m.param;
+      e.u_dst = nullptr; e.o_src = update[j];
+      e.ld_wide = m.cols; e.wide_rows = static_cast<int32_t>(m.rows); e.wide_cols = static_cast<int32_t>(m.cols);
+      e.tall = 0; e.src_dtype = update_dtype; e.wide_dtype = update_dtype; e.param_dtype = m.param_dtype;
+      e.scale_idx = -1;
+      e.aligned = (m.cols % 4 == 0) && aligned16(m.param);
+      e.user_index = j;
+      e.blk_wide = 0; e.blk_stored = blk[j];
+      e.lr_eff = lr_eff_of(hp->lr, m.rows, m.cols);
+      e.decay = decay;
+    }
+  });
+  if (st) return st;
+  DMUON_HIP_TRY(launch_update(reinterpret_cast<const EwMat*>(ws), n, blocks, 0, nullptr, stream));
+  return DMUON_OK;
+}
+
+// ---- measurement hooks -------------------------------------------------------
+
+int dmuon_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = true;
+  return DMUON_OK;
+}
+
+int64_t dmuon_profile_end(char* buf, size_t buf_len) {
+  std::vector<ProfRec> recs;
+  bool was_on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    was_on = g_prof_on;
+    g_prof_on = false;
+    recs.swap(g_prof);
+  }
+  static std::string last_report = "{\"kernels\": {}}";
+  if (!was_on && recs.empty()) {
+    // no profiling window open: hand out the last report again
+    if (buf && buf_len) {
+      const size_t k = std::min(buf_len - 1, last_report.size());
+      std::memcpy(buf, last_report.data(), k);
+      buf[k] = '\0';
+    }
+    return static_cast<int64_t>(last_report.size());
+  }
+  int64_t count[PK_COUNT] = {}, flops[PK_COUNT] = {}, bytes[PK_COUNT] = {};
+  double ms[PK_COUNT] = {};
+  int status = DMUON_OK;
+  for (auto& r : recs) {
+    float t = 0.f;
+    if (status == DMUON_OK) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+      if (e != hipSuccess) status = fail(DMUON_ERR_HIP, std::string("profile events: ") + hipGetErrorString(e));
+    }
+    count[r.kind] += 1;
+    ms[r.kind] += t;
+    flops[r.kind] += r.flops;
+    bytes[r.kind] += r.bytes;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  if (status != DMUON_OK) return status;
+  std::ostringstream os;
+  os.precision(9);
+  os << "{\"kernels\": {";
+  bool first = true;
+  for (int k = 0; k < PK_COUNT; ++k) {
+    if (!count[k]) continue;
+    os << (first ? "" : ", ") << "\"" << kProfNames[k] << "\": {\"launches\": " << count[k]
+       << ", \"ms\": " << ms[k] << ", \"flops\": " << flops[k] << ", \"bytes\": " << bytes[k] << "}";
+    first = false;
+  }
+  os << "}}";
+  last_report = os.str();
+  if (buf && buf_len) {
+    const size_t k = std::min(buf_len - 1, last_report.size());
+    std::memcpy(buf, last_report.data(), k);
+    buf[k] = '\0';
+  }
+  return static_cast<int64_t>(last_report.size());
+}
+
+// ---- plan description (host only) -------------------------------------------
+
+int64_t dmuon_plan_describe(const int64_t* rows, const int64_t* cols, int32_t n, const dmuon_hparams_t* hp,
+                            char* buf, size_t buf_len) {
+  g_last_error.clear();
+  Coeffs cf;
+  std::shared_ptr<Plan> plan;
+  int st = ortho_prepare(rows, cols, n, hp, &cf, &plan);
+  if (st) return st;
+  std::ostringstream os;
+  os << "{\"n\": " << n;
+  if (n > 0) {
+    const Plan& P = *plan;
+    os << ", \"tile\": " << P.tile << ", \"ns_steps\": " << P.ns_steps
+       << ", \"workspace_bytes\": " << P.ws_bytes
+       << ", \"elementwise_blocks\": {\"wide\": " << P.blocks_wide << ", \"stored\": " << P.blocks_stored << "}"
+       << ", \"matrices\": [";
+    for (int i = 0; i < P.n; ++i) {
+      const MatLayout& L = P.mats[i];
+      os << (i ? ", " : "") << "{\"rows\": " << L.rows << ", \"cols\": " << L.cols
+         << ", \"form\": \"" << (L.form == FORM_GRAM ? "gram" : "direct") << "\""
+         << ", \"tall\": " << (L.tall ? "true" : "false")
+         << ", \"m_pad\": " << L.mp << ", \"n_pad\": " << L.np << "}";
+    }
+    os << "], \"launches\": [";
+    for (size_t j = 0; j < P.launches.size(); ++j) {
+      const Launch& l = P.launches[j];
+      int64_t flops = 0;
+      int64_t kmax = 0, kmin = INT64_MAX;
+      for (int q = 0; q < l.count; ++q) {
+        const Op& o = P.ops[l.first + q];
+        flops += 2 * op_tiles(o) * P.tile * P.tile * o.K;
+        kmax = std::max<int64_t>(kmax, o.K);
+        kmin = std::min<int64_t>(kmin, o.K);
+      }
+      os << (j ? ", " : "") << "{\"kind\": \"" << (l.kind == GemmKind::NT ? "NT" : "NN")
+         << "\", \"tasks\": " << l.count << ", \"tiles\": " << l.tiles
+         << ", \"k_max\": " << kmax << ", \"k_min\": " << kmin << ", \"flops\": " << flops << "}";
+    }
+    os << "]";
+  }
+  os << "}";
+  const std::string s = os.str();
+  if (buf && buf_len) {
+    const size_t k = std::min(buf_len - 1, s.size());
+    std::memcpy(buf, s.data(), k);
+    buf[k] = '\0';
+  }
+  return static_cast<int64_t>(s.size());
+}
+
+}  // extern "C"

@@ -1,0 +1,319 @@
+// HBM-bound elementwise kernels of the owner-side Muon step (gfx950).
+//
+//   momentum_kernel  buf <- mu*buf + g; U <- g + mu*buf (Nesterov) or buf,
+//                    written in the wide orientation with zero padding, plus
+//                    one partial sum of U^2 per block (DMuon Training Guide,
+//                    Hyperparameter Guide: momentum and nesterov rows).
+//   finalize_kernel  per-matrix fp64 sum of the partials and the NS input
+//                    scale 1/(||U||_F + eps).
+//   update_kernel    W <- W*(1 - lr*wd) - lr*0.2*sqrt(max(m,n))*O (lr row of
+//                    the same table), or a plain store of O.
+//
+// Each block owns one 64 x 64 element tile of one matrix; a block finds its
+// matrix by binary search over per-matrix first-block indices, so one launch
+// covers a whole ragged batch.  Tall matrices go through a padded LDS tile so
+// that both the stored-orientation and the wide-orientation accesses stay
+// coalesced.  Arithmetic is fp32; bf16 results are rounded to nearest even.
+#include "internal.h"
+
+namespace dmuon {
+namespace {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float load1(const void* p, int64_t i, int dt) {
+  return dt == DT_F32 ? static_cast<const float*>(p)[i]
+                      : bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+__device__ __forceinline__ void store1(void* p, int64_t i, int dt, float v) {
+  if (dt == DT_F32)
+    static_cast<float*>(p)[i] = v;
+  else
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+}
+
+// Four consecutive elements starting at i (i multiple of 4, base aligned).
+__device__ __forceinline__ float4 load4(const void* p, int64_t i, int dt) {
+  if (dt == DT_F32) return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ void store4(void* p, int64_t i, int dt, float4 v) {
+  if (dt == DT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+  } else {
+    uint2 o;
+    o.x = f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16);
+    o.y = f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = o;
+  }
+}
+
+__device__ __forceinline__ float get(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ int find_mat(const EwMat* __restrict__ m, int n, int64_t b, bool stored) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t s = stored ? m[mid].blk_stored : m[mid].blk_wide;
+    if (s <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Thread t of a block covers tile rows (t >> 4) + 16p, p = 0..3, and the four
+// columns 4*(t & 15) .. +3.
+constexpr int kRowsPerPass = kEwThreads / 16;
+constexpr int kPasses = kEwTile / kRowsPerPass;
+
+__global__ void __launch_bounds__(kEwThreads)
+momentum_kernel(const EwMat* __restrict__ mats, int nmats, int mode, float mu, int nesterov,
+                float* __restrict__ partials) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ float red[kEwThreads / 64];
+
+  const int64_t b = blockIdx.x;
+  const int mi = find_mat(mats, nmats, b, false);
+  const EwMat M = mats[mi];
+  const int64_t local = b - M.blk_wide;
+  const int tiles_c = (M.wide_cols + kEwTile - 1) / kEwTile;
+  const int64_t i0 = (local / tiles_c) * kEwTile;   // wide tile origin
+  const int64_t j0 = (local % tiles_c) * kEwTile;
+  const int64_t r0 = M.tall ? j0 : i0;                // stored tile origin
+  const int64_t c0 = M.tall ? i0 : j0;
+
+  const int t = threadIdx.x;
+  const int lc = (t & 15) * 4;
+  const int lr0 = t >> 4;
+
+  float u[kPasses][4];
+  float ss = 0.f;
+  const bool full = M.aligned && r0 + kEwTile <= M.rows && c0 + kEwTile <= M.cols;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t r = r0 + lr0 + kRowsPerPass * p;
+    const int64_t base = r * M.cols + c0 + lc;
+    if (full) {
+      const float4 g = load4(M.src, base, M.src_dtype);
+      float4 uu;
+      if (mode == 0) {
+        const float4 m = *reinterpret_cast<const float4*>(M.mom + base);
+        float4 mn;
+        mn.x = fmaf(mu, m.x, g.x); mn.y = fmaf(mu, m.y, g.y);
+        mn.z = fmaf(mu, m.z, g.z); mn.w = fmaf(mu, m.w, g.w);
+        *reinterpret_cast<float4*>(M.mom + base) = mn;
+        if (nesterov) {
+          uu.x = fmaf(mu, mn.x, g.x); uu.y = fmaf(mu, mn.y, g.y);
+          uu.z = fmaf(mu, mn.z, g.z); uu.w = fmaf(mu, mn.w, g.w);
+        } else {
+          uu = mn;
+        }
+      } else {
+        uu = g;
+      }
+      u[p][0] = uu.x; u[p][1] = uu.y; u[p][2] = uu.z; u[p][3] = uu.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t c = c0 + lc + e;
+        float v = 0.f;
+        if (r < M.rows && c < M.cols) {
+          const int64_t idx = r * M.cols + c;
+          const float g = load1(M.src, idx, M.src_dtype);
+          if (mode == 0) {
+            const float mn = fmaf(mu, M.mom[idx], g);
+            M.mom[idx] = mn;
+            v = nesterov ? fmaf(mu, mn, g) : mn;
+          } else {
+            v = g;
+          }
+        }
+        u[p][e] = v;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss = fmaf(u[p][e], u[p][e], ss);
+  }
+
+  // write U in the wide orientation
+  if (M.tall) {
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tile[lr0 + kRowsPerPass * p][lc + e] = u[p][e];
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[p][e] = tile[lc + e][lr0 + kRowsPerPass * p];
+  }
+  const bool wfull = (M.ld_wide % 4) == 0 && i0 + kEwTile <= M.wide_rows && j0 + kEwTile <= M.wide_cols;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t i = i0 + lr0 + kRowsPerPass * p;
+    const int64_t base = i * M.ld_wide + j0 + lc;
+    if (wfull) {
+      store4(M.u_dst, base, M.wide_dtype, make_float4(u[p][0], u[p][1], u[p][2], u[p][3]));
+    } else if (i < M.wide_rows) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + lc + e < M.wide_cols) store1(M.u_dst, base + e, M.wide_dtype, u[p][e]);
+    }
+  }
+
+  // block sum of U^2
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  if (t == 0) partials[b] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void __launch_bounds__(256)
+finalize_kernel(const EwMat* __restrict__ mats, int nmats, int64_t nblocks,
+                const float* __restrict__ partials, double* __restrict__ sumsq,
+                float* __restrict__ scale, double eps) {
+  __shared__ double red[256];
+  const int mi = blockIdx.x;
+  const int64_t b0 = mats[mi].blk_wide;
+  const int64_t b1 = mi + 1 < nmats ? mats[mi + 1].blk_wide : nblocks;
+  double acc = 0.0;
+  for (int64_t b = b0 + threadIdx.x; b < b1; b += 256) acc += static_cast<double>(partials[b]);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double v = red[0];
+    if (sumsq) sumsq[mats[mi].user_index] = v;
+    if (scale) scale[mi] = static_cast<float>(1.0 / (sqrt(v) + eps));
+  }
+}
+
+__global__ void __launch_bounds__(kEwThreads)
+update_kernel(const EwMat* __restrict__ mats, int nmats, int mode, const float* __restrict__ scale) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
+
+  const int64_t b = blockIdx.x;
+  const int mi = find_mat(mats, nmats, b, true);
+  const EwMat M = mats[mi];
+  const int64_t local = b - M.blk_stored;
+  const int tiles_c = static_cast<int>((M.cols + kEwTile - 1) / kEwTile);
+  const int64_t r0 = (local / tiles_c) * kEwTile;   // stored tile origin
+  const int64_t c0 = (local % tiles_c) * kEwTile;
+
+  const int t = threadIdx.x;
+  const int lc = (t & 15) * 4;
+  const int lr0 = t >> 4;
+  const float osc = M.scale_idx >= 0 ? scale[M.scale_idx] : 1.0f;
+
+  // O for the stored tile: o[p][e] = O(r0 + lr0 + 16p, c0 + lc + e)
+  float o[kPasses][4];
+  {
+    // the wide buffer is read along its rows: wide (a, b) with
+    // a = stored row (not tall) / stored col (tall)
+    const int64_t a0 = M.tall ? c0 : r0;
+    const int64_t bb0 = M.tall ? r0 : c0;
+    const int64_t a_lim = M.tall ? M.cols : M.rows;
+    const int64_t b_lim = M.tall ? M.rows : M.cols;
+    const bool full = (M.ld_wide % 4) == 0 && a0 + kEwTile <= a_lim && bb0 + kEwTile <= b_lim;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int64_t a = a0 + lr0 + kRowsPerPass * p;
+      const int64_t base = a * M.ld_wide + bb0 + lc;
+      if (full) {
+        const float4 v = load4(M.o_src, base, M.wide_dtype);
+        o[p][0] = v.x; o[p][1] = v.y; o[p][2] = v.z; o[p][3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[p][e] = (a < a_lim && bb0 + lc + e < b_lim) ? load1(M.o_src, base + e, M.wide_dtype) : 0.f;
+      }
+    }
+    if (M.tall) {
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[lr0 + kRowsPerPass * p][lc + e] = o[p][e];
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[p][e] = tile[lc + e][lr0 + kRowsPerPass * p];
+    }
+  }
+
+  const float step = M.lr_eff * osc;
+  const bool full = M.aligned && r0 + kEwTile <= M.rows && c0 + kEwTile <= M.cols;
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int64_t r = r0 + lr0 + kRowsPerPass * p;
+    const int64_t base = r * M.cols + c0 + lc;
+    if (full) {
+      float4 res;
+      if (mode == 0) {
+        const float4 w = load4(M.param, base, M.param_dtype);
+        res.x = fmaf(-step, o[p][0], w.x * M.decay);
+        res.y = fmaf(-step, o[p][1], w.y * M.decay);
+        res.z = fmaf(-step, o[p][2], w.z * M.decay);
+        res.w = fmaf(-step, o[p][3], w.w * M.decay);
+      } else {
+        res = make_float4(osc * o[p][0], osc * o[p][1], osc * o[p][2], osc * o[p][3]);
+      }
+      store4(M.param, base, M.param_dtype, res);
+    } else if (r < M.rows) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c0 + lc + e >= M.cols) continue;
+        float res;
+        if (mode == 0)
+          res = fmaf(-step, o[p][e], load1(M.param, base + e, M.param_dtype) * M.decay);
+        else
+          res = osc * o[p][e];
+        store1(M.param, base + e, M.param_dtype, res);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode, float mu,
+                           int nesterov, float* partials, hipStream_t stream) {
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(momentum_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kEwThreads), 0,
+                     stream, mats_dev, nmats, mode, mu, nesterov, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const EwMat* mats_dev, int nmats, int64_t nblocks, const float* partials,
+                             double* sumsq, float* scale, double eps, hipStream_t stream) {
+  if (nmats <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(nmats), dim3(256), 0, stream, mats_dev, nmats, nblocks,
+                     partials, sumsq, scale, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode,
+                         const float* scale, hipStream_t stream) {
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kEwThreads), 0,
+                     stream, mats_dev, nmats, mode, scale);
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

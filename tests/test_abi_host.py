@@ -1,0 +1,165 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and its host-only logic (argument checks, workspace sizing,
+the launch planner) behaves.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmuon.h")
+
+
+@pytest.fixture(scope="module")
+def dm():
+    import matrix_optimizer_step_owned_amd as dm
+    return dm
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmuon_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(dm):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(dm._lib, n), n
+        assert n in dm.EXPORTS, f"binding does not wrap {n}"
+    assert set(dm.EXPORTS) == set(names)
+
+
+def test_struct_layout_matches_header(dm):
+    assert ctypes.sizeof(dm.dmuon_matrix_t) == 48
+    assert ctypes.sizeof(dm.dmuon_hparams_t) == 64
+    assert dm.dmuon_hparams_t.eps.offset == 56
+
+
+def test_defaults_match_pages(dm):
+    import json
+    pages = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_hyperparameters.json")))
+    d = dm.dmuon_hparams_default()
+    for k in ("lr", "momentum", "nesterov", "ns_steps", "weight_decay", "ns_backend"):
+        assert d[k] == pages[k], k
+    assert d["eps"] == 1e-7
+
+
+def test_status_strings(dm):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert dm.dmuon_status_string(code)
+    assert dm.dmuon_status_string(-99) == "unknown status"
+    info = dm.dmuon_backend_info()
+    assert info["arch"] == "gfx950" and "gram_rule" in info
+
+
+def _mats(dm, shapes, dtype=1, grad=True):
+    arr = (dm.dmuon_matrix_t * len(shapes))()
+    addr = 1 << 20
+    for i, (r, c) in enumerate(shapes):
+        m = arr[i]
+        m.rows, m.cols = r, c
+        es = 4 if dtype == 0 else 2
+        m.param = addr; addr += r * c * es + 4096
+        m.grad = addr if grad else None; addr += r * c * es + 4096
+        m.momentum = addr; addr += r * c * 4 + 4096
+        m.param_dtype = m.grad_dtype = dtype
+    return arr
+
+
+def _hp(dm, **kw):
+    h, keep = dm._hparams(**kw)
+    return h, keep
+
+
+def test_argument_errors_before_launch(dm):
+    """Invalid arguments return a status before any device work (these calls
+    would fault if they reached a kernel: the pointers are fake)."""
+    lib = dm._lib
+    h, _ = _hp(dm)
+    mats = _mats(dm, [(256, 512)])
+    ws = 1 << 40
+    def call(mats=mats, n=1, hp=h, ws=ws, wsb=1 << 40):
+        return lib.dmuon_step(mats, n, ctypes.byref(hp), ws, wsb, None)
+    assert call(n=-1) == dm.DMUON_ERR_INVALID_ARG
+    bad = _mats(dm, [(0, 512)])
+    assert call(mats=bad) == dm.DMUON_ERR_INVALID_ARG
+    bad = _mats(dm, [(256, 512)])
+    bad[0].param_dtype = 7
+    assert call(mats=bad) == dm.DMUON_ERR_UNSUPPORTED
+    bad = _mats(dm, [(256, 512)])
+    bad[0].momentum = None
+    assert call(mats=bad) == dm.DMUON_ERR_INVALID_ARG
+    for kw in (dict(ns_steps=17), dict(ns_steps=-1), dict(lr=float("nan")), dict(eps=-1.0),
+               dict(ns_backend=5), dict(ns_precision=3), dict(momentum=float("inf")),
+               dict(ns_coeffs=[1.0, 2.0]), dict(ns_coeffs=[1.0, 2.0, float("nan")])):
+        hh, _k = _hp(dm, **kw)
+        assert call(hp=hh) == dm.DMUON_ERR_INVALID_ARG, kw
+    need = lib.dmuon_step_workspace_size(mats, 1, ctypes.byref(h))
+    assert need > 0
+    assert call(ws=None) == dm.DMUON_ERR_WORKSPACE
+    assert call(wsb=need - 1) == dm.DMUON_ERR_WORKSPACE
+    assert call(ws=ws + 8, wsb=need) == dm.DMUON_ERR_INVALID_ARG   # misaligned
+    # aliasing: two matrices share a param; workspace overlapping a grad
+    two = _mats(dm, [(256, 512), (256, 512)])
+    two[1].param = two[0].param
+    assert lib.dmuon_step(two, 2, ctypes.byref(h), ws, 1 << 40, None) == dm.DMUON_ERR_ALIASING
+    assert "overlaps" in dm.dmuon_last_error()
+    assert call(ws=mats[0].grad - (mats[0].grad % 256), wsb=need + 8192) == dm.DMUON_ERR_ALIASING
+    # all gradients NULL: nothing to do, no device touched
+    nog = _mats(dm, [(256, 512)], grad=False)
+    assert call(mats=nog, ws=None, wsb=0) == dm.DMUON_OK
+    assert call(n=0, ws=None, wsb=0) == dm.DMUON_OK
+
+
+def test_workspace_sizes(dm):
+    lib = dm._lib
+    h, _ = _hp(dm)
+    # direct: 2 m x n + 2 m x m bf16; gram (n >= 2m): 2 m x n + 5 m x m
+    sq = dm.dmuon_orthogonalize_workspace_size([(1024, 1024)])
+    wide = dm.dmuon_orthogonalize_workspace_size([(1024, 3072)])
+    assert sq >= 2 * 1024 * 1024 * 2 * 2
+    assert wide >= (2 * 1024 * 3072 + 5 * 1024 * 1024) * 2
+    assert wide < (2 * 1024 * 3072 + 5 * 1024 * 1024) * 2 + (1 << 20)
+    f32 = dm.dmuon_orthogonalize_workspace_size([(1024, 1024)], ns_precision="f32")
+    assert f32 >= 2 * sq - (1 << 20)
+    assert lib.dmuon_apply_update_workspace_size(3) >= 3 * 128
+
+
+def test_plan_forms_and_grouping(dm):
+    import dmuon_inputs as di
+    w = di.workload(1)
+    shapes = [(m.rows, m.cols) for m in w.matrices]
+    plan = dm.dmuon_plan_describe(shapes)
+    forms = [m["form"] for m in plan["matrices"]]
+    # q, o square -> direct; k, v (1024 x 3072), gate/up (tall), down -> gram
+    assert forms == ["direct", "gram", "gram", "direct", "gram", "gram", "gram"]
+    assert [m["tall"] for m in plan["matrices"]] == [False, False, False, False, True, True, False]
+    # one launch per stage and operand form, each covering every matrix at that stage
+    kinds = [l["kind"] for l in plan["launches"]]
+    assert kinds.count("NN") == 5 + 1          # five direct X-updates, one final Gram Q X0
+    first = plan["launches"][0]
+    assert first["tasks"] == 7 and first["kind"] == "NT"
+    # tasks are ordered longest-K first inside a launch
+    assert first["k_max"] == 8192 and first["k_min"] == 3072
+    # executed flops: symmetric products run t(t+1)/2 of the t x t tiles
+    T = plan["tile"]
+    def sym(m, k): t = m // T; return 2 * (t * (t + 1) // 2) * T * T * k
+    def gen(m, n, k): return 2 * m * n * k
+    def direct(m, n): return 5 * (sym(m, n) + sym(m, m) + gen(m, n, m))
+    def gram(m, n): return sym(m, n) + (5 + 4 + 8) * sym(m, m) + gen(m, n, m)
+    expect = 2 * direct(3072, 3072) + 2 * gram(1024, 3072) + 3 * gram(3072, 8192)
+    assert sum(l["flops"] for l in plan["launches"]) == expect
+
+
+def test_plan_all_direct_and_small(dm):
+    plan = dm.dmuon_plan_describe([(256, 512), (1000, 1500), (130, 70)], ns_backend="direct")
+    assert all(m["form"] == "direct" for m in plan["matrices"])
+    m = plan["matrices"]
+    assert (m[1]["m_pad"], m[1]["n_pad"]) == (1024, 1536)
+    assert (m[2]["m_pad"], m[2]["n_pad"]) == (128, 256) and m[2]["tall"]
+    assert len(plan["launches"]) == 15
+    p0 = dm.dmuon_plan_describe([(256, 512)], ns_steps=0)
+    assert p0["launches"] == []
