@@ -30,6 +30,9 @@
  *     propagates into that matrix only.
  *   - Threads: entry points may be called from several host threads; calls
  *     enqueued on different streams must use different workspaces.
+ *   - Environment: DMUON_GEMM_TILE=128 or 256 forces the tile edge of the
+ *     bf16 NS products (default: 256 for large batches, 128 otherwise); it
+ *     changes the workspace size and the summation order, not the method.
  */
 #ifndef DMUON_H
 #define DMUON_H
@@ -64,7 +67,7 @@ typedef enum { DMUON_NS_PREC_BF16 = 0, DMUON_NS_PREC_F32 = 1 } dmuon_ns_prec_t;
 
 /* One owned matrix (the Training Guide's DedicatedParam, owner side). */
 typedef struct {
-  int64_t rows, cols;      /* as stored; both > 0                                 */
+  int64_t rows, cols;      /* as stored; both in 1 .. 2^22                        */
   void* param;             /* device, rows*cols of param_dtype, updated in place  */
   const void* grad;        /* device, rows*cols of grad_dtype; NULL skips the
                               matrix for this step (nothing of it is touched)     */

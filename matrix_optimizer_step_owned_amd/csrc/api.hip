@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -41,6 +42,7 @@ int fail(int status, const std::string& msg) {
 
 constexpr double kDefaultCoeffs[3] = {3.4445, -4.7750, 2.0315};
 constexpr int kMaxNsSteps = 16;
+constexpr int64_t kMaxDim = int64_t(1) << 22;   // tile coordinates are 16-bit
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -104,29 +106,32 @@ Form choose_form(int32_t backend, int64_t m, int64_t n) {
 
 struct MatLayout {
   int64_t rows, cols, m, n, mp, np;
+  int64_t tile;   // GEMM tile edge of this matrix's products (mp, np are multiples)
   bool tall;
   Form form;
-  // byte offsets into the workspace (SIZE_MAX when unused)
-  size_t x0, x1, o, a, b, p, t, q0, q1;
+  // byte offsets into the workspace (SIZE_MAX when unused); *t buffers hold
+  // the transposes (n_pad x m_pad) of the m_pad x n_pad ones
+  size_t x0, x0t, x1, x1t, o, a, b, p, t, q0, q1;
   size_t out;  // where O is left
 };
 
 // One GEMM as planned: pointers are workspace byte offsets.
 struct Op {
-  GemmKind kind;
   int mat;
-  size_t A, B, C, Y;  // Y == SIZE_MAX: none
-  int64_t lda, ldb, ldc, ldy;
+  int tile;
+  size_t A, B, C, Ct, Y;  // Ct, Y == SIZE_MAX: none
+  int64_t lda, ldb, ldc, ldct, ldy;
   int32_t K, tiles_m, tiles_n, sym, alpha_pow, beta_pow, diag_limit;
   float alpha, beta, gamma;
   bool scaled;
 };
 
 struct Launch {
-  GemmKind kind;
+  int tile;
   int first;   // index into Plan::ops (sorted order)
   int count;
   int64_t tiles;
+  int64_t map_first;  // index of this launch's first entry in Plan::tile_map
   int64_t alg_flops;  // true-size flops, symmetric products counted once
   int64_t alg_bytes;  // bytes an ideal kernel moves
 };
@@ -139,31 +144,44 @@ struct Plan {
   std::vector<MatLayout> mats;
   std::vector<Op> ops;            // grouped by launch
   std::vector<Launch> launches;
+  std::vector<TileRef> tile_map;  // all launches' block -> (task, tile) maps
   std::vector<int64_t> blk_wide, blk_stored;
   int64_t blocks_wide = 0, blocks_stored = 0;
   // workspace layout
-  size_t off_ewmats = 0, off_tasks = 0, off_partials = 0, off_sumsq = 0, off_scale = 0;
-  size_t table_bytes = 0;   // EwMat[] + GemmTask[]
+  size_t off_ewmats = 0, off_tasks = 0, off_map = 0, off_partials = 0, off_sumsq = 0, off_scale = 0;
+  size_t table_bytes = 0;   // EwMat[] + GemmTask[] + TileRef[]
   size_t ws_bytes = 0;
 };
 
 size_t kNone = SIZE_MAX;
 
+// DMUON_GEMM_TILE=128|256 forces the bf16 tile edge (0: automatic choice).
+int gemm_tile_override() {
+  const char* v = std::getenv("DMUON_GEMM_TILE");
+  if (!v) return 0;
+  const int t = std::atoi(v);
+  return (t == kTileBf16 || t == kTileBf16Big) ? t : 0;
+}
+
 std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n, int32_t prec,
-                                 int32_t backend, const Coeffs& cf, bool with_ns) {
+                                 int32_t backend, const Coeffs& cf, bool with_ns, int tile_override) {
   auto P = std::make_shared<Plan>();
   P->n = n;
   P->prec = prec;
   P->ns_steps = with_ns ? static_cast<int>(cf.abc.size() / 3) : 0;
-  P->tile = prec == DMUON_NS_PREC_BF16 ? kTileBf16 : kTileF32;
-  const int64_t T = P->tile;
-  const size_t es = prec == DMUON_NS_PREC_BF16 ? 2 : 4;
-  const int K = P->ns_steps;
-
-  // table and scalars first
-  P->off_ewmats = 0;
-  size_t cur = align_up(sizeof(EwMat) * std::max(n, 1));
-  // GEMM ops are planned below; reserve their table space after counting.
+  // Tile edge: fp32 products use 64.  bf16 products use 256 x 256 tiles
+  // (half the LDS traffic per flop of 128 x 128) when the batch is big
+  // enough to keep every CU busy with them -- at least four waves of such
+  // tiles in the first (X X^T) stage -- and 128 otherwise; matrices narrower
+  // than 256 always use 128.
+  int64_t big_tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t t = (std::min(rows[i], cols[i]) + kTileBf16Big - 1) / kTileBf16Big;
+    big_tiles += t * (t + 1) / 2;
+  }
+  bool use_big = prec == DMUON_NS_PREC_BF16 && big_tiles >= kBigTileMinCount;
+  if (prec == DMUON_NS_PREC_BF16 && tile_override != 0) use_big = tile_override == kTileBf16Big;
+  P->tile = prec == DMUON_NS_PREC_BF16 ? (use_big ? kTileBf16Big : kTileBf16) : kTileF32;
   P->blk_wide.resize(n);
   P->blk_stored.resize(n);
   P->mats.resize(n);
@@ -175,10 +193,12 @@ std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n
     L.tall = rows[i] > cols[i];
     L.m = std::min(rows[i], cols[i]);
     L.n = std::max(rows[i], cols[i]);
-    L.mp = with_ns ? round_up(L.m, T) : L.m;
-    L.np = with_ns ? round_up(L.n, T) : L.n;
+    L.tile = prec == DMUON_NS_PREC_BF16 ? ((use_big && L.m >= 256) ? kTileBf16Big : kTileBf16)
+                                        : kTileF32;
+    L.mp = with_ns ? round_up(L.m, L.tile) : L.m;
+    L.np = with_ns ? round_up(L.n, L.tile) : L.n;
     L.form = choose_form(backend, L.m, L.n);
-    L.x0 = L.x1 = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = kNone;
+    L.x0 = L.x0t = L.x1 = L.x1t = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = kNone;
     P->blk_wide[i] = P->blocks_wide;
     P->blocks_wide += ((L.mp + kEwTile - 1) / kEwTile) * ((L.np + kEwTile - 1) / kEwTile);
     P->blk_stored[i] = P->blocks_stored;
@@ -187,83 +207,90 @@ std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n
   return P;  // buffers are laid out by layout_plan()
 }
 
-// Per-matrix stage lists of the NS iteration.
+// Per-matrix stage lists of the NS iteration.  Every product is
+// C = alpha * A B^T (+ beta Y + gamma I) with K-contiguous operands; the
+// m x n operand of the left-multiplications comes from its transpose.
 void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>>>& stages) {
   const int K = P.ns_steps;
-  const int64_t T = P.tile;
   stages.assign(P.n, {});
   for (int i = 0; i < P.n; ++i) {
     MatLayout& L = P.mats[i];
+    const int64_t T = L.tile;
     auto& st = stages[i];
     if (K == 0) { L.out = L.x0; continue; }
     const int32_t tm_mm = static_cast<int32_t>(L.mp / T);
     const int32_t tn_mn = static_cast<int32_t>(L.np / T);
-    auto sym_op = [&](size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int32_t Kdim) {
+    auto base_op = [&]() {
       Op o{};
-      o.kind = GemmKind::NT; o.mat = i;
-      o.A = A; o.B = B; o.C = C; o.Y = Y;
-      o.lda = o.ldb = ldab; o.ldc = L.mp; o.ldy = L.mp;
-      o.K = Kdim; o.tiles_m = o.tiles_n = tm_mm; o.sym = 1;
+      o.mat = i; o.tile = static_cast<int>(T);
+      o.Ct = kNone; o.Y = kNone; o.ldct = 0; o.ldy = 0;
       o.alpha = 1.f; o.beta = 0.f; o.gamma = 0.f; o.diag_limit = 0;
       o.alpha_pow = o.beta_pow = 0; o.scaled = false;
       return o;
     };
+    // symmetric m x m result of two row-major operands with leading dim ldab
+    auto sym_op = [&](size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int64_t Kdim) {
+      Op o = base_op();
+      o.A = A; o.B = B; o.C = C; o.Y = Y;
+      o.lda = o.ldb = ldab; o.ldc = L.mp; o.ldy = L.mp;
+      o.K = static_cast<int32_t>(Kdim); o.tiles_m = o.tiles_n = tm_mm; o.sym = 1;
+      return o;
+    };
+    // m x n result M . X where M is m x m and X^T (n x m) is stored
+    auto left_op = [&](size_t M, size_t Xt, size_t C, size_t Ct) {
+      Op o = base_op();
+      o.A = M; o.B = Xt; o.C = C; o.Ct = Ct;
+      o.lda = L.mp; o.ldb = L.mp; o.ldc = L.np; o.ldct = L.mp;
+      o.K = static_cast<int32_t>(L.mp); o.tiles_m = tm_mm; o.tiles_n = tn_mn; o.sym = 0;
+      return o;
+    };
     if (L.form == FORM_DIRECT) {
+      const size_t xb[2] = {L.x0, L.x1}, xtb[2] = {L.x0t, L.x1t};
       for (int k = 0; k < K; ++k) {
         const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
-        const size_t xin = (k % 2 == 0) ? L.x0 : L.x1;
-        const size_t xout = (k % 2 == 0) ? L.x1 : L.x0;
+        const size_t xin = xb[k % 2], xin_t = xtb[k % 2];
+        const size_t xout = xb[(k + 1) % 2], xout_t = xtb[(k + 1) % 2];
         // A = s^2 X X^T (s folded in on the first step only)
-        Op g = sym_op(xin, xin, L.a, kNone, L.np, static_cast<int32_t>(L.np));
+        Op g = sym_op(xin, xin, L.a, kNone, L.np, L.np);
         if (k == 0) { g.alpha_pow = 2; g.scaled = true; }
         st.push_back({g});
         // B = b A + c A A
-        Op h = sym_op(L.a, L.a, L.b, L.a, L.mp, static_cast<int32_t>(L.mp));
+        Op h = sym_op(L.a, L.a, L.b, L.a, L.mp, L.mp);
         h.alpha = static_cast<float>(c);
         h.beta = static_cast<float>(b);
         st.push_back({h});
-        // X' = a X + B X
-        Op u{};
-        u.kind = GemmKind::NN; u.mat = i;
-        u.A = L.b; u.B = xin; u.C = xout; u.Y = xin;
-        u.lda = L.mp; u.ldb = L.np; u.ldc = L.np; u.ldy = L.np;
-        u.K = static_cast<int32_t>(L.mp); u.tiles_m = tm_mm; u.tiles_n = tn_mn; u.sym = 0;
-        u.alpha = 1.f; u.beta = static_cast<float>(a); u.gamma = 0.f; u.diag_limit = 0;
-        u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0; u.scaled = (k == 0);
+        // X' = a X + B X, and X'^T for the next step's left product
+        Op u = left_op(L.b, xin_t, xout, k + 1 < K ? xout_t : kNone);
+        u.Y = xin; u.ldy = L.np;
+        u.beta = static_cast<float>(a);
+        u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0;
+        u.scaled = (k == 0);
         st.push_back({u});
       }
-      L.out = (K % 2 == 0) ? L.x0 : L.x1;
+      L.out = xb[K % 2];
     } else {
       // R = s^2 X0 X0^T, kept in A
-      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.np, static_cast<int32_t>(L.np));
+      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.np, L.np);
       r.alpha_pow = 2; r.scaled = true;
       st.push_back({r});
       const size_t qbuf[2] = {L.q0, L.q1};
       for (int k = 0; k < K; ++k) {
         const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
         const size_t pk = (k == 0) ? L.q0 : L.p;   // P_0 is Q itself
-        Op pp = sym_op(L.a, L.a, pk, L.a, L.mp, static_cast<int32_t>(L.mp));
+        Op pp = sym_op(L.a, L.a, pk, L.a, L.mp, L.mp);
         pp.alpha = static_cast<float>(c);
         pp.beta = static_cast<float>(b);
         pp.gamma = static_cast<float>(a);
         pp.diag_limit = static_cast<int32_t>(L.m);
         st.push_back({pp});
         std::vector<Op> next;
-        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.mp,
-                                          static_cast<int32_t>(L.mp)));          // Q <- P Q
-        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.mp,
-                                             static_cast<int32_t>(L.mp)));       // T = P A
+        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.mp, L.mp));  // Q <- P Q
+        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.mp, L.mp));                     // T = P A
         if (!next.empty()) st.push_back(next);
-        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.mp,
-                                            static_cast<int32_t>(L.mp))});      // A = T P
+        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.mp, L.mp)});                     // A = T P
       }
-      Op f{};
-      f.kind = GemmKind::NN; f.mat = i;
-      f.A = qbuf[(K - 1) % 2]; f.B = L.x0; f.C = L.o; f.Y = kNone;
-      f.lda = L.mp; f.ldb = L.np; f.ldc = L.np; f.ldy = L.np;
-      f.K = static_cast<int32_t>(L.mp); f.tiles_m = tm_mm; f.tiles_n = tn_mn; f.sym = 0;
-      f.alpha = 1.f; f.beta = 0.f; f.gamma = 0.f; f.diag_limit = 0;
-      f.alpha_pow = 1; f.beta_pow = 0; f.scaled = true;
+      Op f = left_op(qbuf[(K - 1) % 2], L.x0t, L.o, kNone);                                            // O = s Q X0
+      f.alpha_pow = 1; f.scaled = true;
       st.push_back({f});
       L.out = L.o;
     }
@@ -272,6 +299,64 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
 
 int64_t op_tiles(const Op& o) {
   return o.sym ? int64_t(o.tiles_m) * (o.tiles_m + 1) / 2 : int64_t(o.tiles_m) * o.tiles_n;
+}
+
+// Output tiles of one product in the order one XCD walks them: groups of
+// kTileGroup x kTileGroup tiles, group-row by group-row, so consecutive tiles
+// share their A and B panels; symmetric products keep tn >= tm only.
+void op_tile_order(const Op& o, std::vector<std::pair<int, int>>& out) {
+  out.clear();
+  const int G = kTileGroup;
+  for (int bi = 0; bi < o.tiles_m; bi += G)
+    for (int bj = o.sym ? bi : 0; bj < o.tiles_n; bj += G)
+      for (int tm = bi; tm < std::min(bi + G, o.tiles_m); ++tm)
+        for (int tn = bj; tn < std::min(bj + G, o.tiles_n); ++tn)
+          if (!o.sym || tn >= tm) out.emplace_back(tm, tn);
+}
+
+// Block -> tile maps.  The hardware deals the blocks of a launch to the XCDs
+// round-robin (block b runs on XCD b % 8), and each XCD has its own L2.  Every
+// task's tiles are cut into eight contiguous slices of its blocked order, one
+// per XCD, so each XCD gets an equal share of every task (balanced work) made
+// of neighbouring tiles (shared panels).  Each task's remainder tiles go to
+// the XCDs that follow the previous task's remainder, which makes every XCD's
+// list exactly as long as the number of blocks the hardware sends it.
+void build_tile_maps(Plan& P) {
+  P.tile_map.clear();
+  std::vector<std::pair<int, int>> order;
+  for (Launch& l : P.launches) {
+    l.map_first = static_cast<int64_t>(P.tile_map.size());
+    std::vector<std::vector<TileRef>> xl(kNumXcd);
+    int rot = 0;
+    for (int j = 0; j < l.count; ++j) {
+      op_tile_order(P.ops[l.first + j], order);
+      const int64_t cnt = static_cast<int64_t>(order.size());
+      const int64_t q = cnt / kNumXcd;
+      const int r = static_cast<int>(cnt % kNumXcd);
+      int64_t idx = 0;
+      for (int x = 0; x < kNumXcd; ++x) {
+        const int64_t c = q + (((x - rot + kNumXcd) % kNumXcd) < r ? 1 : 0);
+        for (int64_t k = 0; k < c; ++k, ++idx)
+          xl[x].push_back({j, static_cast<uint16_t>(order[idx].first),
+                           static_cast<uint16_t>(order[idx].second)});
+      }
+      rot = (rot + r) % kNumXcd;
+    }
+    // (the per-XCD list sizes match the dealing by construction; keep a
+    // plain task-by-task order if that ever fails)
+    bool sizes_ok = true;
+    for (int x = 0; x < kNumXcd; ++x)
+      sizes_ok = sizes_ok && int64_t(xl[x].size()) == l.tiles / kNumXcd + (x < l.tiles % kNumXcd ? 1 : 0);
+    if (sizes_ok) {
+      for (int64_t b = 0; b < l.tiles; ++b) P.tile_map.push_back(xl[b % kNumXcd][b / kNumXcd]);
+    } else {
+      for (int j = 0; j < l.count; ++j) {
+        op_tile_order(P.ops[l.first + j], order);
+        for (auto& t : order)
+          P.tile_map.push_back({j, static_cast<uint16_t>(t.first), static_cast<uint16_t>(t.second)});
+      }
+    }
+  }
 }
 
 // Lay out workspace buffers and group ops into launches.
@@ -284,8 +369,10 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
     const size_t mm = align_up(size_t(L.mp) * L.mp * es);
     L.x0 = cur; cur += mn;
     if (!with_ns || P.ns_steps == 0) continue;
+    L.x0t = cur; cur += mn;
     if (L.form == FORM_DIRECT) {
       L.x1 = cur; cur += mn;
+      if (P.ns_steps > 1) { L.x1t = cur; cur += mn; }
       L.a = cur; cur += mm;
       L.b = cur; cur += mm;
     } else {
@@ -309,28 +396,28 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   P.ops.clear();
   P.launches.clear();
   for (size_t s = 0; s < max_st; ++s) {
-    for (GemmKind kind : {GemmKind::NT, GemmKind::NN}) {
+    for (int tile : {kTileBf16Big, kTileBf16, kTileF32}) {
       std::vector<Op> group;
       for (auto& st : stages)
         if (s < st.size())
           for (auto& o : st[s])
-            if (o.kind == kind) group.push_back(o);
+            if (o.tile == tile) group.push_back(o);
       if (group.empty()) continue;
       std::stable_sort(group.begin(), group.end(), [](const Op& x, const Op& y) { return x.K > y.K; });
-      Launch l{kind, static_cast<int>(P.ops.size()), static_cast<int>(group.size()), 0, 0, 0};
+      Launch l{tile, static_cast<int>(P.ops.size()), static_cast<int>(group.size()), 0, 0, 0, 0};
       const int64_t es = P.prec == DMUON_NS_PREC_BF16 ? 2 : 4;
       for (auto& o : group) {
         l.tiles += op_tiles(o);
         const MatLayout& L = P.mats[o.mat];
         const int64_t m = L.m, n = L.n;
         const bool has_y = o.Y != kNone;
-        if (o.kind == GemmKind::NT) {
+        if (o.sym) {
           const int64_t kr = (o.K == L.np) ? n : m;   // X X^T reads m x n, others m x m
           l.alg_flops += m * (m + 1) * kr;
           l.alg_bytes += es * (m * kr * (o.A == o.B ? 1 : 2) + (has_y ? m * m : 0) + m * m);
         } else {
           l.alg_flops += 2 * m * n * m;
-          l.alg_bytes += es * (m * m + m * n + (has_y ? m * n : 0) + m * n);
+          l.alg_bytes += es * (m * m + m * n + (has_y ? m * n : 0) + m * n * (o.Ct != kNone ? 2 : 1));
         }
       }
       P.ops.insert(P.ops.end(), group.begin(), group.end());
@@ -338,12 +425,16 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
     }
   }
 
-  // workspace: [EwMat table][GemmTask table][partials][sumsq][scale][matrices]
+  build_tile_maps(P);
+
+  // workspace: [EwMat table][GemmTask table][tile maps][partials][sumsq][scale][matrices]
   size_t off = 0;
   P.off_ewmats = off;
   off += align_up(sizeof(EwMat) * std::max(P.n, 1));
   P.off_tasks = off;
   off += align_up(sizeof(GemmTask) * std::max<size_t>(P.ops.size(), 1));
+  P.off_map = off;
+  off += align_up(sizeof(TileRef) * std::max<size_t>(P.tile_map.size(), 1));
   P.table_bytes = off;
   P.off_partials = off;
   off += align_up(sizeof(float) * std::max<int64_t>(P.blocks_wide, 1));
@@ -352,11 +443,11 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   P.off_scale = off;
   off += align_up(sizeof(float) * std::max(P.n, 1));
   for (auto& L : P.mats) {
-    for (size_t* f : {&L.x0, &L.x1, &L.o, &L.a, &L.b, &L.p, &L.t, &L.q0, &L.q1, &L.out})
+    for (size_t* f : {&L.x0, &L.x0t, &L.x1, &L.x1t, &L.o, &L.a, &L.b, &L.p, &L.t, &L.q0, &L.q1, &L.out})
       if (*f != kNone) *f += off;
   }
   for (auto& o : P.ops)
-    for (size_t* f : {&o.A, &o.B, &o.C, &o.Y})
+    for (size_t* f : {&o.A, &o.B, &o.C, &o.Ct, &o.Y})
       if (*f != kNone) *f += off;
   P.ws_bytes = off + mat_region;
 }
@@ -373,7 +464,8 @@ std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vect
   std::string key;
   key.reserve(32 + rows.size() * 16 + cf.abc.size() * 8);
   auto put = [&](const void* p, size_t n) { key.append(static_cast<const char*>(p), n); };
-  const int32_t hdr[3] = {prec, with_ns ? backend : -1, with_ns ? 1 : 0};
+  const int tile_override = gemm_tile_override();
+  const int32_t hdr[4] = {prec, with_ns ? backend : -1, with_ns ? 1 : 0, tile_override};
   put(hdr, sizeof(hdr));
   const int64_t n = static_cast<int64_t>(rows.size());
   put(&n, sizeof(n));
@@ -385,7 +477,8 @@ std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vect
     auto it = g_plans.find(key);
     if (it != g_plans.end()) return it->second;
   }
-  auto P = build_plan(rows.data(), cols.data(), static_cast<int>(rows.size()), prec, backend, cf, with_ns);
+  auto P = build_plan(rows.data(), cols.data(), static_cast<int>(rows.size()), prec, backend, cf, with_ns,
+                      tile_override);
   layout_plan(*P, cf, with_ns);
   std::lock_guard<std::mutex> lk(g_plan_mu);
   if (g_plans.size() > 256) g_plans.clear();
@@ -472,10 +565,8 @@ int check_device() {
 // measurement hooks
 // ---------------------------------------------------------------------------
 
-enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_NT_BF16, PK_GEMM_NN_BF16, PK_GEMM_NT_F32,
-                PK_GEMM_NN_F32, PK_UPDATE, PK_COUNT };
-const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_nt_bf16", "gemm_nn_bf16",
-                                          "gemm_nt_f32", "gemm_nn_f32", "update"};
+enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_BF16, PK_GEMM_F32, PK_UPDATE, PK_COUNT };
+const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_bf16", "gemm_f32", "update"};
 
 struct ProfRec {
   int kind;
@@ -533,37 +624,35 @@ float lr_eff_of(double lr, int64_t rows, int64_t cols) {
 
 void fill_tasks(const Plan& P, char* ws_base, GemmTask* out) {
   auto ptr = [&](size_t off) -> void* { return off == kNone ? nullptr : ws_base + off; };
-  int64_t first_tile = 0;
   for (const Launch& l : P.launches) {
-    int64_t tile = 0;
     for (int j = 0; j < l.count; ++j) {
       const Op& o = P.ops[l.first + j];
       GemmTask& t = out[l.first + j];
       t.A = ptr(o.A);
       t.B = ptr(o.B);
       t.C = ptr(o.C);
+      t.Ct = ptr(o.Ct);
       t.Y = ptr(o.Y);
       t.scale = o.scaled ? reinterpret_cast<const float*>(ws_base + P.off_scale) + o.mat : nullptr;
-      t.lda = o.lda; t.ldb = o.ldb; t.ldc = o.ldc; t.ldy = o.ldy;
+      t.lda = o.lda; t.ldb = o.ldb; t.ldc = o.ldc; t.ldct = o.ldct; t.ldy = o.ldy;
       t.K = o.K; t.tiles_m = o.tiles_m; t.tiles_n = o.tiles_n; t.sym = o.sym;
       t.alpha_pow = o.alpha_pow; t.beta_pow = o.beta_pow; t.diag_limit = o.diag_limit;
-      t.tile_begin = static_cast<int32_t>(tile);
       t.alpha = o.alpha; t.beta = o.beta; t.gamma = o.gamma;
-      tile += op_tiles(o);
     }
-    (void)first_tile;
   }
+  if (!P.tile_map.empty())
+    std::memcpy(reinterpret_cast<char*>(out) + (P.off_map - P.off_tasks), P.tile_map.data(),
+                sizeof(TileRef) * P.tile_map.size());
 }
 
 int run_gemms(const Plan& P, char* ws, hipStream_t stream) {
   const GemmTask* tasks = reinterpret_cast<const GemmTask*>(ws + P.off_tasks);
+  const TileRef* map = reinterpret_cast<const TileRef*>(ws + P.off_map);
   for (const Launch& l : P.launches) {
     const bool bf = P.prec == DMUON_NS_PREC_BF16;
-    const int kind = bf ? (l.kind == GemmKind::NT ? PK_GEMM_NT_BF16 : PK_GEMM_NN_BF16)
-                        : (l.kind == GemmKind::NT ? PK_GEMM_NT_F32 : PK_GEMM_NN_F32);
-    hipError_t e = prof_launch(kind, l.alg_flops, l.alg_bytes, stream, [&] {
-      return bf ? launch_gemm_bf16(l.kind, tasks + l.first, l.count, l.tiles, P.tile, stream)
-                : launch_gemm_f32(l.kind, tasks + l.first, l.count, l.tiles, P.tile, stream);
+    hipError_t e = prof_launch(bf ? PK_GEMM_BF16 : PK_GEMM_F32, l.alg_flops, l.alg_bytes, stream, [&] {
+      return bf ? launch_gemm_bf16(tasks + l.first, map + l.map_first, l.tiles, l.tile, stream)
+                : launch_gemm_f32(tasks + l.first, map + l.map_first, l.tiles, l.tile, stream);
     });
     if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("GEMM launch: ") + hipGetErrorString(e));
   }
@@ -576,8 +665,8 @@ int check_matrix_fields(const dmuon_matrix_t& m, int i, bool need_grad_mom) {
     std::snprintf(buf, sizeof buf, "matrix %d: rows and cols must be > 0", i);
     return fail(DMUON_ERR_INVALID_ARG, buf);
   }
-  if (m.rows > (1LL << 30) || m.cols > (1LL << 30)) {
-    std::snprintf(buf, sizeof buf, "matrix %d: dimension above 2^30", i);
+  if (m.rows > kMaxDim || m.cols > kMaxDim) {
+    std::snprintf(buf, sizeof buf, "matrix %d: dimension above 2^22", i);
     return fail(DMUON_ERR_INVALID_ARG, buf);
   }
   if (!dtype_ok(m.param_dtype) || !dtype_ok(m.grad_dtype)) {
@@ -723,6 +812,7 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
       e.rows = m.rows; e.cols = m.cols;
       e.src = m.grad; e.mom = m.momentum; e.param = m.param;
       e.u_dst = ws + L.x0; e.o_src = ws + L.out;
+      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.mp;
       e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
       e.tall = L.tall; e.src_dtype = m.grad_dtype; e.wide_dtype = wide_dt; e.param_dtype = m.param_dtype;
       e.scale_idx = P.ns_steps == 0 ? j : -1;
@@ -834,6 +924,7 @@ int dmuon_momentum(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t*
       e.rows = m.rows; e.cols = m.cols;
       e.src = m.grad; e.mom = m.momentum; e.param = nullptr;
       e.u_dst = ns_input[active[j]]; e.o_src = nullptr;
+      e.u_dst_t = nullptr; e.ld_wide_t = 0;
       e.ld_wide = L.n; e.wide_rows = static_cast<int32_t>(L.m); e.wide_cols = static_cast<int32_t>(L.n);
       e.tall = L.tall; e.src_dtype = m.grad_dtype; e.wide_dtype = ns_input_dtype; e.param_dtype = m.param_dtype;
       e.scale_idx = -1;
@@ -861,7 +952,7 @@ static int ortho_prepare(const int64_t* rows, const int64_t* cols, int32_t n, co
   int st = check_hparams(hp, false, cf);
   if (st) return st;
   for (int i = 0; i < n; ++i)
-    if (rows[i] <= 0 || cols[i] <= 0 || rows[i] > (1LL << 30) || cols[i] > (1LL << 30))
+    if (rows[i] <= 0 || cols[i] <= 0 || rows[i] > kMaxDim || cols[i] > kMaxDim)
       return fail(DMUON_ERR_INVALID_ARG, "matrix " + std::to_string(i) + ": bad shape");
   if (n == 0) return DMUON_OK;
   *plan = get_plan(std::vector<int64_t>(rows, rows + n), std::vector<int64_t>(cols, cols + n),
@@ -935,6 +1026,7 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
       e.rows = rows[j]; e.cols = cols[j];
       e.src = in[j]; e.mom = nullptr; e.param = out[j];
       e.u_dst = ws + L.x0; e.o_src = ws + L.out;
+      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.mp;
       e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
       e.tall = L.tall; e.src_dtype = io_dtype; e.wide_dtype = wide_dt; e.param_dtype = io_dtype;
       e.scale_idx = P.ns_steps == 0 ? j : -1;
@@ -1009,6 +1101,7 @@ int dmuon_apply_update(const dmuon_matrix_t* mats, int32_t n, const void* const*
       e.rows = m.rows; e.cols = m.cols;
       e.src = nullptr; e.mom = nullptr; e.param = m.param;
       e.u_dst = nullptr; e.o_src = update[j];
+      e.u_dst_t = nullptr; e.ld_wide_t = 0;
       e.ld_wide = m.cols; e.wide_rows = static_cast<int32_t>(m.rows); e.wide_cols = static_cast<int32_t>(m.cols);
       e.tall = 0; e.src_dtype = update_dtype; e.wide_dtype = update_dtype; e.param_dtype = m.param_dtype;
       e.scale_idx = -1;
@@ -1110,22 +1203,43 @@ int64_t dmuon_plan_describe(const int64_t* rows, const int64_t* cols, int32_t n,
       const MatLayout& L = P.mats[i];
       os << (i ? ", " : "") << "{\"rows\": " << L.rows << ", \"cols\": " << L.cols
          << ", \"form\": \"" << (L.form == FORM_GRAM ? "gram" : "direct") << "\""
-         << ", \"tall\": " << (L.tall ? "true" : "false")
+         << ", \"tall\": " << (L.tall ? "true" : "false") << ", \"tile\": " << L.tile
          << ", \"m_pad\": " << L.mp << ", \"n_pad\": " << L.np << "}";
     }
-    os << "], \"launches\": [";
+    // every launch's map must hit each output tile once, and give XCD x
+    // exactly the blocks b < tiles with b % 8 == x
+    bool map_ok = P.tile_map.size() == [&] { size_t t = 0; for (auto& l : P.launches) t += l.tiles; return t; }();
+    for (const Launch& l : P.launches) {
+      std::vector<std::vector<char>> seen(l.count);
+      for (int j = 0; j < l.count; ++j) {
+        const Op& o = P.ops[l.first + j];
+        seen[j].assign(size_t(o.tiles_m) * o.tiles_n, 0);
+      }
+      for (int64_t b = 0; b < l.tiles && map_ok; ++b) {
+        const TileRef r = P.tile_map[l.map_first + b];
+        if (r.task < 0 || r.task >= l.count) { map_ok = false; break; }
+        const Op& o = P.ops[l.first + r.task];
+        if (r.tm >= o.tiles_m || r.tn >= o.tiles_n || (o.sym && r.tn < r.tm)) { map_ok = false; break; }
+        char& c = seen[r.task][size_t(r.tm) * o.tiles_n + r.tn];
+        if (c) { map_ok = false; break; }
+        c = 1;
+      }
+    }
+    os << "], \"tile_map_valid\": " << (map_ok ? "true" : "false") << ", \"launches\": [";
     for (size_t j = 0; j < P.launches.size(); ++j) {
       const Launch& l = P.launches[j];
       int64_t flops = 0;
       int64_t kmax = 0, kmin = INT64_MAX;
       for (int q = 0; q < l.count; ++q) {
         const Op& o = P.ops[l.first + q];
-        flops += 2 * op_tiles(o) * P.tile * P.tile * o.K;
+        flops += 2 * op_tiles(o) * o.tile * o.tile * o.K;
         kmax = std::max<int64_t>(kmax, o.K);
         kmin = std::min<int64_t>(kmin, o.K);
       }
-      os << (j ? ", " : "") << "{\"kind\": \"" << (l.kind == GemmKind::NT ? "NT" : "NN")
-         << "\", \"tasks\": " << l.count << ", \"tiles\": " << l.tiles
+      int nsym = 0;
+      for (int q = 0; q < l.count; ++q) nsym += P.ops[l.first + q].sym;
+      os << (j ? ", " : "") << "{\"sym_tasks\": " << nsym << ", \"left_tasks\": " << (l.count - nsym)
+         << ", \"tile\": " << l.tile << ", \"tasks\": " << l.count << ", \"tiles\": " << l.tiles
          << ", \"k_max\": " << kmax << ", \"k_min\": " << kmin << ", \"flops\": " << flops << "}";
     }
     os << "]";

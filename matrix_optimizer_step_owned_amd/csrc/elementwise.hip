@@ -147,29 +147,55 @@ momentum_kernel(const EwMat* __restrict__ mats, int nmats, int mode, float mu, i
     for (int e = 0; e < 4; ++e) ss = fmaf(u[p][e], u[p][e], ss);
   }
 
-  // write U in the wide orientation
-  if (M.tall) {
+  // Write U (wide: wide_rows x wide_cols) and/or U^T (wide_cols x wide_rows).
+  // One of the two is the stored orientation of this tile and is written
+  // straight from registers; the other goes through the LDS tile.
+  void* const direct_dst = M.tall ? M.u_dst_t : M.u_dst;
+  void* const trans_dst = M.tall ? M.u_dst : M.u_dst_t;
+  const int64_t direct_ld = M.tall ? M.ld_wide_t : M.ld_wide;
+  const int64_t trans_ld = M.tall ? M.ld_wide : M.ld_wide_t;
+  // extents (rows, cols) of the destinations and this tile's origin in them
+  const int64_t d_rows = M.tall ? M.wide_cols : M.wide_rows, d_cols = M.tall ? M.wide_rows : M.wide_cols;
+  const int64_t d_r0 = M.tall ? j0 : i0, d_c0 = M.tall ? i0 : j0;
+  if (trans_dst) {
 #pragma unroll
     for (int p = 0; p < kPasses; ++p)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tile[lr0 + kRowsPerPass * p][lc + e] = u[p][e];
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kPasses; ++p)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[p][e] = tile[lc + e][lr0 + kRowsPerPass * p];
   }
-  const bool wfull = (M.ld_wide % 4) == 0 && i0 + kEwTile <= M.wide_rows && j0 + kEwTile <= M.wide_cols;
+  if (direct_dst) {
+    const bool dfull = (direct_ld % 4) == 0 && d_r0 + kEwTile <= d_rows && d_c0 + kEwTile <= d_cols;
 #pragma unroll
-  for (int p = 0; p < kPasses; ++p) {
-    const int64_t i = i0 + lr0 + kRowsPerPass * p;
-    const int64_t base = i * M.ld_wide + j0 + lc;
-    if (wfull) {
-      store4(M.u_dst, base, M.wide_dtype, make_float4(u[p][0], u[p][1], u[p][2], u[p][3]));
-    } else if (i < M.wide_rows) {
+    for (int p = 0; p < kPasses; ++p) {
+      const int64_t i = d_r0 + lr0 + kRowsPerPass * p;
+      const int64_t base = i * direct_ld + d_c0 + lc;
+      if (dfull) {
+        store4(direct_dst, base, M.wide_dtype, make_float4(u[p][0], u[p][1], u[p][2], u[p][3]));
+      } else if (i < d_rows) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j0 + lc + e < M.wide_cols) store1(M.u_dst, base + e, M.wide_dtype, u[p][e]);
+        for (int e = 0; e < 4; ++e)
+          if (d_c0 + lc + e < d_cols) store1(direct_dst, base + e, M.wide_dtype, u[p][e]);
+      }
+    }
+  }
+  if (trans_dst) {
+    __syncthreads();
+    // the transposed destination has extents (d_cols, d_rows), origin (d_c0, d_r0)
+    const bool tfull = (trans_ld % 4) == 0 && d_c0 + kEwTile <= d_cols && d_r0 + kEwTile <= d_rows;
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const int64_t i = d_c0 + lr0 + kRowsPerPass * p;
+      const int64_t base = i * trans_ld + d_r0 + lc;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = tile[lc + e][lr0 + kRowsPerPass * p];
+      if (tfull) {
+        store4(trans_dst, base, M.wide_dtype, make_float4(v[0], v[1], v[2], v[3]));
+      } else if (i < d_cols) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (d_r0 + lc + e < d_rows) store1(trans_dst, base + e, M.wide_dtype, v[e]);
+      }
     }
   }
 

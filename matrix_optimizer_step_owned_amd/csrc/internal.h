@@ -22,9 +22,11 @@ struct EwMat {
   const void* src;           // momentum: grad; load: the matrix to orthogonalise
   float* mom;                // momentum buffer (momentum mode), else null
   void* param;               // update: W, in place (param_dtype); store: output
-  void* u_dst;               // momentum/load: U destination (wide)
+  void* u_dst;               // momentum/load: U destination (wide), or null
+  void* u_dst_t;             // momentum/load: U^T destination (wide_cols x wide_rows), or null
   const void* o_src;         // update/store: O source (wide)
   int64_t ld_wide;           // leading dimension of the wide buffers (elements)
+  int64_t ld_wide_t;         // leading dimension of the U^T buffer
   int32_t wide_rows;         // rows of the wide region to write (>= m; zero fill)
   int32_t wide_cols;         // cols of the wide region to write (>= n; zero fill)
   int32_t tall;              // rows > cols
@@ -41,31 +43,45 @@ struct EwMat {
   float decay;               // 1 - lr * weight_decay
 };
 
-// One GEMM of a grouped launch.  C = alpha_eff * (A . op(B)) + beta_eff * Y
-// + gamma * I[i == j < diag_limit], with alpha_eff = alpha * s^alpha_pow and
-// beta_eff = beta * s^beta_pow, s = *scale (1 when scale is null).
-//   A: row-major, K contiguous (lda), rows = tiles_m * tile
-//   op(B): NT kernels read B as row-major N x K (K contiguous);
-//          NN kernels read B as row-major K x N (N contiguous).
-// All extents are padded to whole tiles with zeros, so kernels do no bounds
-// checks.  sym: the result is symmetric; only tiles with tm <= tn are
-// computed and each is also written mirrored.
+// One GEMM of a grouped launch: C[i][j] = alpha_eff * sum_k A[i][k] B[j][k]
+// + beta_eff * Y[i][j] + gamma * [i == j < diag_limit], with
+// alpha_eff = alpha * s^alpha_pow, beta_eff = beta * s^beta_pow and
+// s = *scale (1 when scale is null).  A (M x K) and B (N x K) are row-major
+// with K contiguous.  All extents are padded to whole tiles with zeros, so
+// kernels do no bounds checks.
+//   sym: the result is symmetric; only tiles with tm <= tn are computed and
+//        the upper triangle is also written mirrored, so C is exactly
+//        symmetric.
+//   Ct:  if not null, C^T is also written there (N x M, ldct).
 struct GemmTask {
   const void* A;
   const void* B;
   void* C;
+  void* Ct;
   const void* Y;
   const float* scale;
-  int64_t lda, ldb, ldc, ldy;
+  int64_t lda, ldb, ldc, ldct, ldy;
   int32_t K;
   int32_t tiles_m, tiles_n;
   int32_t sym;
   int32_t alpha_pow, beta_pow;
   int32_t diag_limit;
-  int32_t tile_begin;        // index of this task's first tile in the launch
   float alpha, beta, gamma;
-  int32_t pad_;
 };
+
+// One block of a grouped GEMM launch: which task and which output tile.
+// Block b of a launch processes map[b]; the host orders the map so that the
+// blocks the hardware sends to one XCD (b % 8 == x) cover a contiguous, 2-D
+// blocked part of every task, sharing operand panels in that XCD's L2.
+struct TileRef {
+  int32_t task;
+  uint16_t tm, tn;
+};
+
+// Number of XCDs that workgroups are dealt to round-robin, and the edge of
+// the square groups of tiles walked together inside a task.
+constexpr int kNumXcd = 8;
+constexpr int kTileGroup = 4;
 
 // ---- launchers (each enqueues one kernel on `stream`) ----------------------
 
@@ -83,15 +99,17 @@ hipError_t launch_finalize(const EwMat* mats_dev, int nmats, int64_t nblocks,
 hipError_t launch_update(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode,
                          const float* scale, hipStream_t stream);
 
-// Grouped NS products.  tile = 128 (bf16) or 64 (fp32).
-enum class GemmKind { NT, NN };
-hipError_t launch_gemm_bf16(GemmKind kind, const GemmTask* tasks_dev, int ntasks,
-                            int64_t ntiles, int tile, hipStream_t stream);
-hipError_t launch_gemm_f32(GemmKind kind, const GemmTask* tasks_dev, int ntasks,
-                           int64_t ntiles, int tile, hipStream_t stream);
+// Grouped NS products.  tile = 128 or 256 (bf16), 64 (fp32).
+hipError_t launch_gemm_bf16(const GemmTask* tasks_dev, const TileRef* map_dev, int64_t ntiles,
+                            int tile, hipStream_t stream);
+hipError_t launch_gemm_f32(const GemmTask* tasks_dev, const TileRef* map_dev, int64_t ntiles,
+                           int tile, hipStream_t stream);
 
-// Tile edge of the grouped GEMM kernels per precision.
+// Tile edges of the grouped GEMM kernels.
 constexpr int kTileBf16 = 128;
+constexpr int kTileBf16Big = 256;
 constexpr int kTileF32 = 64;
+// 256-tiles are used when the first NS stage has at least this many of them.
+constexpr int64_t kBigTileMinCount = 1024;
 
 }  // namespace dmuon

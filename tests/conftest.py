@@ -28,3 +28,14 @@ def lib():
         pytest.skip("no GPU")
     import matrix_optimizer_step_owned_amd as dm
     return dm
+
+
+@pytest.fixture(params=["auto", "256"])
+def gemm_tile(request, monkeypatch):
+    """Run a GPU test with the library's own tile choice and with the
+    256 x 256 bf16 tiles forced (DMUON_GEMM_TILE)."""
+    if request.param == "auto":
+        monkeypatch.delenv("DMUON_GEMM_TILE", raising=False)
+    else:
+        monkeypatch.setenv("DMUON_GEMM_TILE", request.param)
+    return request.param

@@ -121,8 +121,11 @@ def test_workspace_sizes(dm):
     sq = dm.dmuon_orthogonalize_workspace_size([(1024, 1024)])
     wide = dm.dmuon_orthogonalize_workspace_size([(1024, 3072)])
     assert sq >= 2 * 1024 * 1024 * 2 * 2
-    assert wide >= (2 * 1024 * 3072 + 5 * 1024 * 1024) * 2
-    assert wide < (2 * 1024 * 3072 + 5 * 1024 * 1024) * 2 + (1 << 20)
+    # Gram form: X0, X0^T and O (m x n), A, P, T, Q0, Q1 (m x m)
+    assert wide >= (3 * 1024 * 3072 + 5 * 1024 * 1024) * 2
+    assert wide < (3 * 1024 * 3072 + 5 * 1024 * 1024) * 2 + (1 << 20)
+    # direct form: X0, X0^T, X1, X1^T (m x n), A, B (m x m)
+    assert sq >= (4 * 1024 * 1024 + 2 * 1024 * 1024) * 2
     f32 = dm.dmuon_orthogonalize_workspace_size([(1024, 1024)], ns_precision="f32")
     assert f32 >= 2 * sq - (1 << 20)
     assert lib.dmuon_apply_update_workspace_size(3) >= 3 * 128
@@ -137,11 +140,13 @@ def test_plan_forms_and_grouping(dm):
     # q, o square -> direct; k, v (1024 x 3072), gate/up (tall), down -> gram
     assert forms == ["direct", "gram", "gram", "direct", "gram", "gram", "gram"]
     assert [m["tall"] for m in plan["matrices"]] == [False, False, False, False, True, True, False]
-    # one launch per stage and operand form, each covering every matrix at that stage
-    kinds = [l["kind"] for l in plan["launches"]]
-    assert kinds.count("NN") == 5 + 1          # five direct X-updates, one final Gram Q X0
+    # one launch per stage, each covering every matrix at that stage: 16 Gram
+    # stages; the direct form's 15 fit inside them
+    assert len(plan["launches"]) == 16
+    left = [l["left_tasks"] for l in plan["launches"]]
+    assert sum(1 for v in left if v) == 5 + 1   # five direct X-updates, one final Gram Q X0
     first = plan["launches"][0]
-    assert first["tasks"] == 7 and first["kind"] == "NT"
+    assert first["tasks"] == 7 and first["sym_tasks"] == 7
     # tasks are ordered longest-K first inside a launch
     assert first["k_max"] == 8192 and first["k_min"] == 3072
     # executed flops: symmetric products run t(t+1)/2 of the t x t tiles
@@ -161,5 +166,35 @@ def test_plan_all_direct_and_small(dm):
     assert (m[1]["m_pad"], m[1]["n_pad"]) == (1024, 1536)
     assert (m[2]["m_pad"], m[2]["n_pad"]) == (128, 256) and m[2]["tall"]
     assert len(plan["launches"]) == 15
+    assert all(l["sym_tasks"] + l["left_tasks"] == l["tasks"] for l in plan["launches"])
     p0 = dm.dmuon_plan_describe([(256, 512)], ns_steps=0)
     assert p0["launches"] == []
+
+
+def test_plan_tile_choice(dm):
+    import dmuon_inputs as di
+    big = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(2).matrices])
+    assert big["tile"] == 256 and all(m["tile"] == 256 for m in big["matrices"])
+    assert all(m["m_pad"] % 256 == 0 and m["n_pad"] % 256 == 0 for m in big["matrices"])
+    # the 196 matrices still form one launch per stage and operand form
+    assert len(big["launches"]) == 16 and big["launches"][0]["tasks"] == 196
+    small = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(1).matrices])
+    assert small["tile"] == 128
+    # in a big batch, matrices narrower than 256 keep 128-tiles in launches of their own
+    mixed = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(2).matrices] + [(128, 2048)])
+    assert mixed["matrices"][-1]["tile"] == 128 and mixed["matrices"][-1]["m_pad"] == 128
+    assert {l["tile"] for l in mixed["launches"]} == {128, 256}
+    assert dm.dmuon_plan_describe([(4096, 4096)], ns_precision="f32")["tile"] == 64
+
+
+def test_tile_maps_cover_every_tile_once(dm):
+    import dmuon_inputs as di
+    cases = [[(m.rows, m.cols) for m in di.workload(k).matrices] for k in (1, 2, 4)]
+    cases.append([(1000, 1500), (130, 70), (2048, 128), (64, 64), (1, 300)])
+    for shapes in cases:
+        for extra in ({}, {"ns_backend": "direct"}, {"ns_precision": "f32"}):
+            plan = dm.dmuon_plan_describe(shapes, **extra)
+            assert plan["tile_map_valid"] is True, (len(shapes), extra)
+    # the element count must fit the 16-bit tile coordinates
+    with pytest.raises(dm.DmuonError):
+        dm.dmuon_plan_describe([(1 << 23, 16)])

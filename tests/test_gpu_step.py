@@ -61,7 +61,7 @@ def test_step_small_workload(lib, prec, backend):
 
 
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
-def test_step_ragged_multi_step(lib, prec):
+def test_step_ragged_multi_step(lib, prec, gemm_tile):
     """A mixed batch (wide, tall, square, ragged tails, bf16 and fp32
     parameters) over three steps, each matrix tracked by the oracle."""
     specs = [(256, 512, "bf16"), (768, 256, "f32"), (1000, 1500, "bf16"), (384, 384, "f32"),
@@ -91,7 +91,7 @@ def test_step_ragged_multi_step(lib, prec):
             assert rel(f64(moms[i]), m_new) <= 1e-6, (step, i)
             err = check_param_step(f64(params[i]), w_before[i], w_ref, dt, NS_TOL[prec], prec,
                                    what=f"step {step} matrix {i} {r}x{c}")
-            print(f"step {step} {r}x{c} {dt} ns={prec}: update rel err {err:.3e}")
+            print(f"step {step} {r}x{c} {dt} ns={prec} tile={gemm_tile}: update rel err {err:.3e}")
 
 
 def test_step_nan_isolation_and_skip(lib):
