@@ -106,6 +106,7 @@ Form choose_form(int32_t backend, int64_t m, int64_t n) {
 
 struct MatLayout {
   int64_t rows, cols, m, n, mp, np;
+  int64_t pm, pn; // row pitches (elements) of the buffers whose rows hold mp / np values
   int64_t tile;   // GEMM tile edge of this matrix's products (mp, np are multiples)
   bool tall;
   Form form;
@@ -197,6 +198,11 @@ std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n
                                         : kTileF32;
     L.mp = with_ns ? round_up(L.m, L.tile) : L.m;
     L.np = with_ns ? round_up(L.n, L.tile) : L.n;
+    // one extra 128-byte line per row: rows of a power-of-two-like pitch
+    // would otherwise start at the same offsets of the L2 channel
+    // interleave, and a k-slice of a panel would land on a few channels
+    L.pm = with_ns ? L.mp + kPitchPad : L.mp;
+    L.pn = with_ns ? L.np + kPitchPad : L.np;
     L.form = choose_form(backend, L.m, L.n);
     L.x0 = L.x0t = L.x1 = L.x1t = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = kNone;
     P->blk_wide[i] = P->blocks_wide;
@@ -232,7 +238,7 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
     auto sym_op = [&](size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int64_t Kdim) {
       Op o = base_op();
       o.A = A; o.B = B; o.C = C; o.Y = Y;
-      o.lda = o.ldb = ldab; o.ldc = L.mp; o.ldy = L.mp;
+      o.lda = o.ldb = ldab; o.ldc = L.pm; o.ldy = L.pm;
       o.K = static_cast<int32_t>(Kdim); o.tiles_m = o.tiles_n = tm_mm; o.sym = 1;
       return o;
     };
@@ -240,7 +246,7 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
     auto left_op = [&](size_t M, size_t Xt, size_t C, size_t Ct) {
       Op o = base_op();
       o.A = M; o.B = Xt; o.C = C; o.Ct = Ct;
-      o.lda = L.mp; o.ldb = L.mp; o.ldc = L.np; o.ldct = L.mp;
+      o.lda = L.pm; o.ldb = L.pm; o.ldc = L.pn; o.ldct = L.pm;
       o.K = static_cast<int32_t>(L.mp); o.tiles_m = tm_mm; o.tiles_n = tn_mn; o.sym = 0;
       return o;
     };
@@ -251,17 +257,17 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
         const size_t xin = xb[k % 2], xin_t = xtb[k % 2];
         const size_t xout = xb[(k + 1) % 2], xout_t = xtb[(k + 1) % 2];
         // A = s^2 X X^T (s folded in on the first step only)
-        Op g = sym_op(xin, xin, L.a, kNone, L.np, L.np);
+        Op g = sym_op(xin, xin, L.a, kNone, L.pn, L.np);
         if (k == 0) { g.alpha_pow = 2; g.scaled = true; }
         st.push_back({g});
         // B = b A + c A A
-        Op h = sym_op(L.a, L.a, L.b, L.a, L.mp, L.mp);
+        Op h = sym_op(L.a, L.a, L.b, L.a, L.pm, L.mp);
         h.alpha = static_cast<float>(c);
         h.beta = static_cast<float>(b);
         st.push_back({h});
         // X' = a X + B X, and X'^T for the next step's left product
         Op u = left_op(L.b, xin_t, xout, k + 1 < K ? xout_t : kNone);
-        u.Y = xin; u.ldy = L.np;
+        u.Y = xin; u.ldy = L.pn;
         u.beta = static_cast<float>(a);
         u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0;
         u.scaled = (k == 0);
@@ -270,24 +276,24 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
       L.out = xb[K % 2];
     } else {
       // R = s^2 X0 X0^T, kept in A
-      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.np, L.np);
+      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.pn, L.np);
       r.alpha_pow = 2; r.scaled = true;
       st.push_back({r});
       const size_t qbuf[2] = {L.q0, L.q1};
       for (int k = 0; k < K; ++k) {
         const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
         const size_t pk = (k == 0) ? L.q0 : L.p;   // P_0 is Q itself
-        Op pp = sym_op(L.a, L.a, pk, L.a, L.mp, L.mp);
+        Op pp = sym_op(L.a, L.a, pk, L.a, L.pm, L.mp);
         pp.alpha = static_cast<float>(c);
         pp.beta = static_cast<float>(b);
         pp.gamma = static_cast<float>(a);
         pp.diag_limit = static_cast<int32_t>(L.m);
         st.push_back({pp});
         std::vector<Op> next;
-        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.mp, L.mp));  // Q <- P Q
-        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.mp, L.mp));                     // T = P A
+        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.pm, L.mp));  // Q <- P Q
+        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.pm, L.mp));                     // T = P A
         if (!next.empty()) st.push_back(next);
-        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.mp, L.mp)});                     // A = T P
+        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.pm, L.mp)});                     // A = T P
       }
       Op f = left_op(qbuf[(K - 1) % 2], L.x0t, L.o, kNone);                                            // O = s Q X0
       f.alpha_pow = 1; f.scaled = true;
@@ -302,54 +308,64 @@ int64_t op_tiles(const Op& o) {
 }
 
 // Output tiles of one product in the order one XCD walks them: groups of
-// kTileGroup x kTileGroup tiles, group-row by group-row, so consecutive tiles
-// share their A and B panels; symmetric products keep tn >= tm only.
+// kTileGroupRows x kTileGroupCols tiles, group-row by group-row, so the tiles
+// an XCD runs at once share their A and B panels; symmetric products keep
+// tn >= tm only.
 void op_tile_order(const Op& o, std::vector<std::pair<int, int>>& out) {
   out.clear();
-  const int G = kTileGroup;
-  for (int bi = 0; bi < o.tiles_m; bi += G)
-    for (int bj = o.sym ? bi : 0; bj < o.tiles_n; bj += G)
-      for (int tm = bi; tm < std::min(bi + G, o.tiles_m); ++tm)
-        for (int tn = bj; tn < std::min(bj + G, o.tiles_n); ++tn)
+  const int GR = kTileGroupRows, GC = kTileGroupCols;
+  for (int bi = 0; bi < o.tiles_m; bi += GR)
+    for (int bj = o.sym ? (bi / GC) * GC : 0; bj < o.tiles_n; bj += GC)
+      for (int tm = bi; tm < std::min(bi + GR, o.tiles_m); ++tm)
+        for (int tn = bj; tn < std::min(bj + GC, o.tiles_n); ++tn)
           if (!o.sym || tn >= tm) out.emplace_back(tm, tn);
 }
 
 // Block -> tile maps.  The hardware deals the blocks of a launch to the XCDs
-// round-robin (block b runs on XCD b % 8), and each XCD has its own L2.  Every
-// task's tiles are cut into eight contiguous slices of its blocked order, one
-// per XCD, so each XCD gets an equal share of every task (balanced work) made
-// of neighbouring tiles (shared panels).  Each task's remainder tiles go to
-// the XCDs that follow the previous task's remainder, which makes every XCD's
-// list exactly as long as the number of blocks the hardware sends it.
+// round-robin (block b runs on XCD b % 8), and each XCD has its own L2, so
+// the blocks an XCD runs at once should be neighbouring tiles of one task.
+// Tasks (longest k first, then largest) go whole to the XCD with the most
+// room left; a task larger than that room is split, so every XCD's list is
+// exactly as long as the number of blocks the hardware sends it and every
+// XCD gets a like mix of short and long tasks.
 void build_tile_maps(Plan& P) {
   P.tile_map.clear();
   std::vector<std::pair<int, int>> order;
   for (Launch& l : P.launches) {
     l.map_first = static_cast<int64_t>(P.tile_map.size());
+    int64_t room[kNumXcd];
+    for (int x = 0; x < kNumXcd; ++x) room[x] = l.tiles / kNumXcd + (x < l.tiles % kNumXcd ? 1 : 0);
+    std::vector<int> idx(l.count);
+    for (int j = 0; j < l.count; ++j) idx[j] = j;
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) {
+      const Op& oa = P.ops[l.first + a];
+      const Op& ob = P.ops[l.first + b];
+      if (oa.K != ob.K) return oa.K > ob.K;
+      return op_tiles(oa) > op_tiles(ob);
+    });
     std::vector<std::vector<TileRef>> xl(kNumXcd);
-    int rot = 0;
-    for (int j = 0; j < l.count; ++j) {
+    bool ok = true;
+    for (int j : idx) {
       op_tile_order(P.ops[l.first + j], order);
-      const int64_t cnt = static_cast<int64_t>(order.size());
-      const int64_t q = cnt / kNumXcd;
-      const int r = static_cast<int>(cnt % kNumXcd);
-      int64_t idx = 0;
-      for (int x = 0; x < kNumXcd; ++x) {
-        const int64_t c = q + (((x - rot + kNumXcd) % kNumXcd) < r ? 1 : 0);
-        for (int64_t k = 0; k < c; ++k, ++idx)
-          xl[x].push_back({j, static_cast<uint16_t>(order[idx].first),
-                           static_cast<uint16_t>(order[idx].second)});
+      size_t pos = 0;
+      while (pos < order.size()) {
+        int x = 0;
+        for (int y = 1; y < kNumXcd; ++y)
+          if (room[y] > room[x]) x = y;
+        if (room[x] <= 0) { ok = false; break; }
+        const size_t take = std::min<size_t>(static_cast<size_t>(room[x]), order.size() - pos);
+        for (size_t k = 0; k < take; ++k, ++pos)
+          xl[x].push_back({j, static_cast<uint16_t>(order[pos].first), static_cast<uint16_t>(order[pos].second)});
+        room[x] -= static_cast<int64_t>(take);
       }
-      rot = (rot + r) % kNumXcd;
+      if (!ok) break;
     }
-    // (the per-XCD list sizes match the dealing by construction; keep a
-    // plain task-by-task order if that ever fails)
-    bool sizes_ok = true;
-    for (int x = 0; x < kNumXcd; ++x)
-      sizes_ok = sizes_ok && int64_t(xl[x].size()) == l.tiles / kNumXcd + (x < l.tiles % kNumXcd ? 1 : 0);
-    if (sizes_ok) {
+    for (int x = 0; x < kNumXcd; ++x) ok = ok && room[x] == 0;
+    if (ok) {
       for (int64_t b = 0; b < l.tiles; ++b) P.tile_map.push_back(xl[b % kNumXcd][b / kNumXcd]);
     } else {
+      // (cannot happen: the rooms add up to the tile count; a plain
+      // task-by-task order keeps the map valid regardless)
       for (int j = 0; j < l.count; ++j) {
         op_tile_order(P.ops[l.first + j], order);
         for (auto& t : order)
@@ -365,14 +381,15 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   // buffers
   size_t cur = 0;  // relative to the start of the matrix region
   for (auto& L : P.mats) {
-    const size_t mn = align_up(size_t(L.mp) * L.np * es);
-    const size_t mm = align_up(size_t(L.mp) * L.mp * es);
+    const size_t mn = align_up(size_t(L.mp) * L.pn * es);    // m x n, pitch pn
+    const size_t mnt = align_up(size_t(L.np) * L.pm * es);   // n x m, pitch pm
+    const size_t mm = align_up(size_t(L.mp) * L.pm * es);    // m x m, pitch pm
     L.x0 = cur; cur += mn;
     if (!with_ns || P.ns_steps == 0) continue;
-    L.x0t = cur; cur += mn;
+    L.x0t = cur; cur += mnt;
     if (L.form == FORM_DIRECT) {
       L.x1 = cur; cur += mn;
-      if (P.ns_steps > 1) { L.x1t = cur; cur += mn; }
+      if (P.ns_steps > 1) { L.x1t = cur; cur += mnt; }
       L.a = cur; cur += mm;
       L.b = cur; cur += mm;
     } else {
@@ -812,8 +829,8 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
       e.rows = m.rows; e.cols = m.cols;
       e.src = m.grad; e.mom = m.momentum; e.param = m.param;
       e.u_dst = ws + L.x0; e.o_src = ws + L.out;
-      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.mp;
-      e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
+      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.pm;
+      e.ld_wide = L.pn; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
       e.tall = L.tall; e.src_dtype = m.grad_dtype; e.wide_dtype = wide_dt; e.param_dtype = m.param_dtype;
       e.scale_idx = P.ns_steps == 0 ? j : -1;
       e.aligned = (m.cols % 4 == 0) && aligned16(m.grad) && aligned16(m.momentum) && aligned16(m.param);
@@ -1026,8 +1043,8 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
       e.rows = rows[j]; e.cols = cols[j];
       e.src = in[j]; e.mom = nullptr; e.param = out[j];
       e.u_dst = ws + L.x0; e.o_src = ws + L.out;
-      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.mp;
-      e.ld_wide = L.np; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
+      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.pm;
+      e.ld_wide = L.pn; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
       e.tall = L.tall; e.src_dtype = io_dtype; e.wide_dtype = wide_dt; e.param_dtype = io_dtype;
       e.scale_idx = P.ns_steps == 0 ? j : -1;
       e.aligned = (cols[j] % 4 == 0) && aligned16(in[j]) && aligned16(out[j]);

@@ -32,6 +32,7 @@
 // fp32 kernel (the fp32 NS mode): 64 x 64 x 16 tiles, four waves of 32 x 32,
 // v_mfma_f32_32x32x2f32, register-staged k-major LDS.
 #include <cstdlib>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -124,17 +125,56 @@ __device__ __forceinline__ void store_fragment(const f32x16_t& a, OutT* __restri
 // bf16
 // ---------------------------------------------------------------------------
 
-constexpr int kStageK = 32;                     // k per LDS stage
-constexpr int kRowBytes = kStageK * 2;          // 64
+constexpr int kStageK = 64;                     // k per LDS stage
+constexpr int kRowBytes = kStageK * 2;          // 128: one cache line per row
 constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows filled by one wave-wide DMA load
 
-// Column swizzle of the fp32 staging tile (row r, column c at r*BT + (c ^
-// stage_swz(r))): conflict-free for the accumulator writes (32 columns of rows
-// r and r+4 per instruction), the row reads (two aligned 16-byte pieces per
-// 8 columns) and the column reads (16 row-groups x 4 columns).
-__device__ __forceinline__ int stage_swz(int r) { return (((r >> 3) & 15) << 2) ^ (((r >> 2) & 1) << 5); }
+// Swizzle of the bf16 staging tile: 16-byte chunk c of staged row r sits at
+// chunk c ^ stg_swz(r).  The staging writes (8 bytes of 32 consecutive rows
+// per half-wave) then spread over 16 chunk positions, the row reads (16
+// chunks of one row per 16 lanes) are a permutation, and the column reads
+// (8 bytes of rows 8b + e, b = 0..15, per half-wave) hit 16 different chunk
+// positions.
+__device__ __forceinline__ int stg_swz(int r) { return (r ^ (r >> 3)) & 15; }
 
-__device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ (((row >> 1) ^ (row >> 2)) & 3); }
+// Two fp32 values rounded to nearest-even bf16, packed (first in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#define GLOBAL_AS __attribute__((address_space(1)))
+
+// Global-address-space accesses (flat ones would also count against the LDS
+// counter that the LDS-only barrier waits on).
+__device__ __forceinline__ u32x4_t gload_u32x4(const void* p) {
+  return *reinterpret_cast<const GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ void gstore_u32x4(void* p, u32x4_t v) {
+  *reinterpret_cast<GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p)) = v;
+}
+__device__ __forceinline__ void gstore_u16(void* p, uint16_t v) {
+  *reinterpret_cast<GLOBAL_AS uint16_t*>(reinterpret_cast<uintptr_t>(p)) = v;
+}
+__device__ __forceinline__ float gload_f32(const float* p) {
+  return *reinterpret_cast<const GLOBAL_AS float*>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Workgroup barrier that orders LDS only: global stores already issued stay
+// in flight (__syncthreads would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Operand rows in LDS are 128 bytes (eight 16-byte chunks); chunk c of row r
+// sits in slot c ^ ((r >> 1) & 7).  A fragment read (16 lanes of a 128-bit
+// read per cycle: 16 consecutive rows, one chunk) then covers all 64 banks.
+__device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 template <int BT, int kStages>
 __global__ void __launch_bounds__(256)
@@ -153,6 +193,17 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   const int tm = ref.tm, tn = ref.tn;
   const GemmTask& T = tasks[ref.task];
   const int nk = T.K / kStageK;
+  // everything the epilogue needs from the task, read before the main loop
+  const float s_scale = T.scale ? gload_f32(T.scale) : 1.f;
+  const float alpha = T.alpha * spow(s_scale, T.alpha_pow);
+  const float beta = T.beta * spow(s_scale, T.beta_pow);
+  const float gamma = T.gamma;
+  const int diag_limit = T.diag_limit;
+  uint16_t* const C = static_cast<uint16_t*>(T.C);
+  uint16_t* const Ct = static_cast<uint16_t*>(T.Ct);
+  const uint16_t* const Y = static_cast<const uint16_t*>(T.Y);
+  const int64_t ldc = T.ldc, ldct = T.ldct, ldy = T.ldy;
+  const int mode = T.sym ? (tm != tn ? 1 : 2) : (Ct ? 3 : 0);   // 0 plain, 1 mirror, 2 diagonal, 3 Ct
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -160,7 +211,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
 
   // DMA sources: load q of this wave fills LDS block idx = wave + 4q of the
   // stage (blocks 0 .. LOADS_PER_OP-1: A rows, the rest: B rows); lane l
-  // writes slot l%4 of row 16*block + l/4, which holds chunk slot^swizzle.
+  // writes slot l%8 of row 8*block + l/8, which holds chunk slot^swizzle.
   const uint16_t* src[LOADS];
   int dst_off[LOADS];
 #pragma unroll
@@ -168,20 +219,23 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     const int idx = wave + 4 * q;
     const bool is_b = idx >= LOADS_PER_OP;
     const int blk = is_b ? idx - LOADS_PER_OP : idx;
-    const int row = blk * kRowsPerLoad + (lane >> 2);
-    const int chunk = slot_of(row, lane & 3);
+    const int row = blk * kRowsPerLoad + (lane >> 3);
+    const int chunk = slot_of(row, lane & 7);
     const uint16_t* base = is_b ? static_cast<const uint16_t*>(T.B) + (int64_t(tn) * BT + row) * T.ldb
                                 : static_cast<const uint16_t*>(T.A) + (int64_t(tm) * BT + row) * T.lda;
     src[q] = base + chunk * 8;
     dst_off[q] = (is_b ? OPB : 0) + blk * 1024;
   }
 
-  // fragment read offsets (bytes within a stage) for the two k-halves
-  int frag_off[2];
+  // fragment read offsets (bytes within a stage) for the four k-quarters:
+  // lanes 0-31 take chunk 2kq, lanes 32-63 chunk 2kq+1 of rows lane & 31
+  // (the swizzle depends on the row bits below 16 only, so one offset serves
+  // every 32-row fragment)
+  int frag_off[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kq = 0; kq < 4; ++kq) {
     const int r = lane & 31;
-    frag_off[kk] = r * kRowBytes + slot_of(r, kk * 2 + (lane >> 5)) * 16;
+    frag_off[kq] = r * kRowBytes + slot_of(r, kq * 2 + (lane >> 5)) * 16;
   }
 
   f32x16_t acc[F][F];
@@ -200,8 +254,8 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
                                        (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
   };
-  auto read_frags = [&](int s, int kk, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F]) {
-    const char* st = smem + (s % kStages) * STB + frag_off[kk];
+  auto read_frags = [&](int s, int kq, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F]) {
+    const char* st = smem + (s % kStages) * STB + frag_off[kq];
 #pragma unroll
     for (int i = 0; i < F; ++i)
       fa[i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * WT + i * 32) * kRowBytes);
@@ -214,177 +268,242 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     for (int i = 0; i < F; ++i)
 #pragma unroll
       for (int j = 0; j < F; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        // B fragment first: the lane then holds row (lane & 31) of its
+        // 32 x 32 block and, in register 4g + r, column 8g + 4(lane >> 5) + r
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
-
-  // The loop is branch-free: past the last stage, loads re-fetch the last
-  // stage's data (in bounds) into buffers that are never read again, and the
-  // fragment reads re-read the last stage, so every iteration issues the
-  // same number of loads and the wait counts are constants.
-  // prologue: stages 0 .. kStages-2 in flight, then stage 0 complete
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_stage(s < nk ? s : nk - 1, s);
-  wait_vmcnt<LOADS * (kStages - 2)>();
-  __builtin_amdgcn_s_barrier();
 
   // Instruction order is pinned with scheduling groups (the compiler would
   // otherwise sink each fragment read to just before its first use): the
   // in-order issue must never run out of independent MFMAs while loads and
   // LDS reads are issued.
   constexpr int kMfma = 0x008, kVmem = 0x010, kDsRead = 0x100;
-  constexpr int NFRAG = 2 * F;          // fragment reads per half-stage
-  constexpr int NMFMA = F * F;          // MFMAs per half-stage
+  constexpr int NFRAG = 2 * F;          // fragment reads per k-quarter
+  constexpr int NMFMA = F * F;          // MFMAs per k-quarter
   bf16x8_t fa0[F], fb0[F], fa1[F], fb1[F];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // phase A: first k-half of stage kt; the second half's fragments load
-    read_frags(kt, 1, fa1, fb1);
-    mfmas(fa0, fb0);
+  // one k-quarter: MFMAs on (fa, fb) while the next quarter's fragments load
+  auto quarter = [&](int s, int kq_next, bf16x8_t (&na)[F], bf16x8_t (&nb)[F],
+                     const bf16x8_t (&fa)[F], const bf16x8_t (&fb)[F]) {
+    read_frags(s, kq_next, na, nb);
+    mfmas(fa, fb);
 #pragma unroll
     for (int i = 0; i < NFRAG; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kMfma, NMFMA - NFRAG, 0);
+    if (NMFMA > NFRAG) __builtin_amdgcn_sched_group_barrier(kMfma, NMFMA - NFRAG, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // stage kt+1 complete in this wave (kStages-3 later stages in flight),
-    // then in every wave; all waves are past stage kt-1, whose buffer the
-    // next load overwrites
-    wait_vmcnt<LOADS * (kStages - 3)>();
-    __builtin_amdgcn_s_barrier();
+  };
+
+  // Ring of kStages stages, 64 k each.  Stage kt's data sits in slot kt %
+  // kStages.  Per stage: quarters 0-2 run on fragments already in registers
+  // while the next quarter's load; then one barrier, at which stage kt+1 has
+  // landed (own loads counted, everyone's by the barrier) and every wave has
+  // finished its LDS reads of stage kt; quarter 3 then issues the loads of
+  // stage kt+kStages into stage kt's slot and the reads of stage kt+1's
+  // first quarter.  The loop is branch-free: past the last stage, loads
+  // re-fetch the last stage (in bounds, same bytes) and fragment reads
+  // re-read it, so the wait counts are constants.
+#pragma unroll
+  for (int s = 0; s < kStages; ++s) issue_stage(s < nk ? s : nk - 1, s);
+  wait_vmcnt<LOADS * (kStages - 1)>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    quarter(kt, 1, fa1, fb1, fa0, fb0);
+    quarter(kt, 2, fa0, fb0, fa1, fb1);
+    quarter(kt, 3, fa1, fb1, fa0, fb0);
+    wait_vmcnt<LOADS * (kStages - 2)>();
+    lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // phase B: second k-half of stage kt; loads for stage kt+kStages-1 and
-    // the first-half fragments of stage kt+1 are issued in between
-    const int ahead = kt + kStages - 1;
-    issue_stage(ahead < nk ? ahead : nk - 1, ahead);
+    // (the reads come first in program order: the compiler keeps LDS reads
+    // and direct-to-LDS loads in program order)
     read_frags(kt + 1 < nk ? kt + 1 : nk - 1, 0, fa0, fb0);
+    const int ahead = kt + kStages;
+    issue_stage(ahead < nk ? ahead : nk - 1, ahead);
     mfmas(fa1, fb1);
+    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, 16 loads
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-    }
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+      }
 #pragma unroll
-    for (int i = 0; i < NFRAG; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-      if (LOADS + i < NMFMA) __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+      }
+    } else {                             // 4 MFMAs, 4 reads, 8 loads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+      }
     }
-    if (NMFMA > LOADS + NFRAG) __builtin_amdgcn_sched_group_barrier(kMfma, NMFMA - LOADS - NFRAG, 1);
+    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && LOADS == 16)
+                            : (NMFMA == 4 && NFRAG == 4 && LOADS == 8), "schedule");
     __builtin_amdgcn_sched_barrier(0);
   }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
 
-  // Epilogue through LDS (the ring is free once the loads have drained): the
-  // accumulators are staged in fp32, then written out with 16-byte,
-  // row-contiguous stores -- C row by row, and the mirror (symmetric tiles)
-  // or the transposed copy Ct column by column of the staged tile.
-  __syncthreads();
-  const float s = T.scale ? *T.scale : 1.f;
-  const float alpha = T.alpha * spow(s, T.alpha_pow);
-  const float beta = T.beta * spow(s, T.beta_pow);
-  const float gamma = T.gamma;
-  const int diag_limit = T.diag_limit;
-  uint16_t* __restrict__ C = static_cast<uint16_t*>(T.C);
-  uint16_t* __restrict__ Ct = static_cast<uint16_t*>(T.Ct);
-  const uint16_t* __restrict__ Y = static_cast<const uint16_t*>(T.Y);
-  const int64_t ldc = T.ldc, ldct = T.ldct, ldy = T.ldy;
-  const int mode = T.sym ? (tm != tn ? 1 : 2) : (Ct ? 3 : 0);   // 0 plain, 1 mirror, 2 diagonal, 3 Ct
-  uint16_t* const Tdst = mode == 3 ? Ct : C;
-  const int64_t ldt = mode == 3 ? ldct : ldc;
-
+  // Epilogue.  The ring holds the finished tile as bf16, row-major, 16-byte
+  // chunks swizzled per row (stg_swz).  Each lane scales its accumulators
+  // (and adds beta*Y, which a Y tile first brings into the same place by
+  // direct-to-LDS loads, and gamma on the diagonal), rounds them to bf16 in
+  // pairs and writes 8 bytes per 4 columns.  C then leaves row by row in
+  // 16-byte pieces; the mirror (symmetric tiles) or the transposed copy Ct
+  // leaves column by column: a lane reads 4 columns of 8 rows (8 x 8 bytes)
+  // and transposes them in registers into 4 pieces of 16 bytes.  Global
+  // accesses use global (not flat) instructions and the barriers order LDS
+  // only, so stores stay in flight until the block ends; LDS reads are
+  // issued in batches ahead of their use.
   constexpr int RING = kStages * STB;
-  constexpr int ROWS = RING >= BT * BT * 4 ? BT : WT;   // staged rows per pass
-  static_assert(RING >= WT * BT * 4, "staging does not fit");
-  constexpr int CPR = BT / 8;                           // 8-wide chunks per staged row
-  constexpr int CH = ROWS / 8;                          // 8-long chunks per transposed row
-  float* const stg = reinterpret_cast<float*>(smem);
+  static_assert(RING >= BT * BT * 2, "staging does not fit");
+  constexpr int NCH = BT / 8;                    // 16-byte chunks per staged row
+  constexpr int ROWB = BT * 2;                   // bytes per staged row
+  char* const stg = smem;
   const int t = threadIdx.x;
+  const int h = lane >> 5;
 
-  for (int pass = 0; pass < BT / ROWS; ++pass) {
-    const int r_lo = pass * ROWS;
-    if (pass > 0) __syncthreads();
-    if (wm * WT >= r_lo && wm * WT < r_lo + ROWS) {
+  lds_barrier();                                 // every wave is done with the ring
+  if (Y) {
+    // Y tile into the staging layout: one 1 KB load covers 1024 / ROWB rows
+    constexpr int RPL = 1024 / ROWB;
+    constexpr int NLOAD = BT * ROWB / 1024 / 4;  // per wave
 #pragma unroll
-      for (int i = 0; i < F; ++i)
+    for (int q = 0; q < NLOAD; ++q) {
+      const int first = (wave + 4 * q) * RPL;
+      const int row = first + lane / NCH;
+      const int chunk = (lane % NCH) ^ stg_swz(row);
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(Y + (int64_t(tm) * BT + row) * ldy + int64_t(tn) * BT + chunk * 8),
+          (LDS_AS void*)(stg + first * ROWB), 16, 0, 0);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  // scale, add, round and stage: fragment (i, j), register group g covers
+  // row wm*WT + 32i + (lane & 31), columns wn*WT + 32j + 8g + 4(lane >> 5) + 0..3
+  {
+    const bool has_y = Y != nullptr;
+    const bool add_gamma = tm == tn && gamma != 0.f && wm == wn;
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+    for (int i = 0; i < F; ++i) {
+      const int row = wm * WT + i * 32 + (lane & 31);
+      const int sw = stg_swz(row);
+      char* const srow = stg + row * ROWB + h * 8;
+      const bool diag_row = int64_t(tm) * BT + row < diag_limit;
+#pragma unroll
+      for (int j = 0; j < F; ++j) {
+        uint2 y[4];
+        if (has_y) {
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int r = wm * WT - r_lo + i * 32 + (lane >> 5) * 4 + g * 8 + rr;
-              const int c = wn * WT + j * 32 + (lane & 31);
-              stg[r * BT + (c ^ stage_swz(r))] = alpha * acc[i][j][g * 4 + rr];
-            }
-    }
-    __syncthreads();
-
-    // rows: thread t covers chunk t % CPR of staged rows t / CPR + (256 / CPR) k
-#pragma unroll 4
-    for (int k = 0; k < ROWS * CPR / 256; ++k) {
-      const int lr = t / CPR + (256 / CPR) * k;
-      const int c0 = (t % CPR) * 8;
-      const int rt = r_lo + lr;                 // row within the tile
-      const int64_t R = int64_t(tm) * BT + rt;  // row within C
-      const int64_t C0 = int64_t(tn) * BT + c0;
-      float* const lo = stg + lr * BT + ((c0 ^ stage_swz(lr)) & ~3);
-      float* const hi = stg + lr * BT + (((c0 + 4) ^ stage_swz(lr)) & ~3);
-      float4 a = *reinterpret_cast<const float4*>(lo);
-      float4 b = *reinterpret_cast<const float4*>(hi);
-      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      if (Y) {
-        const uint4 y = *reinterpret_cast<const uint4*>(Y + R * ldy + C0);
-        const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = fmaf(beta, bf16_bits_to_f32((yw[e >> 1] >> ((e & 1) * 16)) & 0xffffu), v[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] += (R == C0 + e && R < diag_limit) ? gamma : 0.f;
-      if (mode != 0) {
-        *reinterpret_cast<float4*>(lo) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(hi) = make_float4(v[4], v[5], v[6], v[7]);
-      }
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_bits(v[e]);
-      uint16_t* dst = C + R * ldc + C0;
-      if (mode != 2 || c0 >= rt) {
-        *reinterpret_cast<uint4*>(dst) =
-            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-      } else if (c0 + 7 >= rt) {   // diagonal tile: upper triangle only
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c0 + e >= rt) dst[e] = static_cast<uint16_t>(h[e]);
-      }
-    }
-
-    // transposed: thread t covers chunk t % CH (8 staged rows) of staged
-    // column t / CH + (256 / CH) k
-    if (mode != 0) {
-      __syncthreads();
-#pragma unroll 4
-      for (int k = 0; k < BT * CH / 256; ++k) {
-        const int c = t / CH + (256 / CH) * k;   // column within the tile
-        const int q = t % CH;
-        const int r0 = 8 * q;                    // first staged row
-        uint32_t h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = f32_to_bf16_bits(stg[(r0 + i) * BT + (c ^ stage_swz(r0 + i))]);
-        uint16_t* dst = Tdst + (int64_t(tn) * BT + c) * ldt + int64_t(tm) * BT + r_lo + r0;
-        const int rt0 = r_lo + r0;               // tile row of element i = rt0 + i
-        if (mode != 2 || rt0 + 7 < c) {
-          *reinterpret_cast<uint4*>(dst) =
-              make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-        } else if (rt0 < c) {      // diagonal tile: strict lower triangle only
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (rt0 + i < c) dst[i] = static_cast<uint16_t>(h[i]);
+            y[g] = *reinterpret_cast<const uint2*>(srow + ((((wn * WT + j * 32) / 8 + g) ^ sw) << 4));
         }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = alpha * acc[i][j][4 * g + r];
+          if (has_y) {
+            v[0] = fmaf(beta, __uint_as_float(y[g].x << 16), v[0]);
+            v[1] = fmaf(beta, __uint_as_float(y[g].x & 0xffff0000u), v[1]);
+            v[2] = fmaf(beta, __uint_as_float(y[g].y << 16), v[2]);
+            v[3] = fmaf(beta, __uint_as_float(y[g].y & 0xffff0000u), v[3]);
+          }
+          if (i == j && add_gamma) {             // wm == wn: the tile diagonal
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] += ((lane & 31) == 8 * g + 4 * h + r && diag_row) ? gamma : 0.f;
+          }
+          *reinterpret_cast<uint2*>(srow + ((((wn * WT + j * 32) / 8 + g) ^ sw) << 4)) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);       // bounds the live accumulator copies
       }
     }
   }
+  lds_barrier();
+
+  // C, row by row: thread t covers chunk t % NCH of rows t / NCH + (256 / NCH) k
+  auto rows_out = [&](auto diag_tile) {
+    constexpr bool kD = decltype(diag_tile)::value;
+    constexpr int NIT = BT * NCH / 256, BATCH = 4;
+    const int chunk = t % NCH;
+    const int c0 = chunk * 8;
+    uint16_t* const cbase = C + (int64_t(tm) * BT) * ldc + int64_t(tn) * BT + c0;
+#pragma unroll
+    for (int k0 = 0; k0 < NIT; k0 += BATCH) {
+      u32x4_t v[BATCH];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int row = t / NCH + (256 / NCH) * (k0 + b);
+        v[b] = *reinterpret_cast<const u32x4_t*>(stg + row * ROWB + ((chunk ^ stg_swz(row)) << 4));
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int row = t / NCH + (256 / NCH) * (k0 + b);
+        uint16_t* const dst = cbase + int64_t(row) * ldc;
+        if (!kD || c0 >= row) {
+          gstore_u32x4(dst, v[b]);
+        } else if (c0 + 7 >= row) {              // diagonal tile: upper triangle only
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c0 + e >= row) gstore_u16(dst + e, static_cast<uint16_t>(v[b][e >> 1] >> ((e & 1) * 16)));
+        }
+      }
+    }
+  };
+  if (mode == 2) rows_out(std::true_type{});
+  else rows_out(std::false_type{});
+
+  // mirror / Ct, column by column: a lane takes rows 8rb..8rb+7 of columns
+  // 8cc + 4hf + 0..3 and writes them as rows of the destination
+  auto cols_out = [&](auto diag_tile, uint16_t* const Tdst, const int64_t ldt) {
+    constexpr bool kD = decltype(diag_tile)::value;
+    constexpr int LPC = 2 * (BT / 8);            // lanes per column chunk
+#pragma unroll 2
+    for (int q = 0; q < BT * BT * 2 / 64 / 256; ++q) {
+      const int tq = t + 256 * q;
+      const int cc = tq / LPC;
+      const int rb = (tq % LPC) >> 1;
+      const int hf = tq & 1;
+      uint2 w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = 8 * rb + e;
+        w[e] = *reinterpret_cast<const uint2*>(stg + row * ROWB + ((cc ^ stg_swz(row)) << 4) + hf * 8);
+      }
+      const int r0 = 8 * rb;
+#pragma unroll
+      for (int sc = 0; sc < 4; ++sc) {           // destination row: tile column 8cc + 4hf + sc
+        const int col = 8 * cc + 4 * hf + sc;
+        const uint32_t sel = (sc & 1) ? 0x07060302u : 0x05040100u;
+        u32x4_t o;
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const uint32_t lo = (sc >> 1) ? w[2 * p2].y : w[2 * p2].x;
+          const uint32_t hi = (sc >> 1) ? w[2 * p2 + 1].y : w[2 * p2 + 1].x;
+          o[p2] = __builtin_amdgcn_perm(hi, lo, sel);
+        }
+        uint16_t* const dst = Tdst + (int64_t(tn) * BT + col) * ldt + int64_t(tm) * BT + r0;
+        if (!kD || r0 + 7 < col) {
+          gstore_u32x4(dst, o);
+        } else if (r0 < col) {                   // diagonal tile: strict lower triangle only
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (r0 + e < col) gstore_u16(dst + e, static_cast<uint16_t>(o[e >> 1] >> ((e & 1) * 16)));
+        }
+      }
+    }
+  };
+  if (mode == 1) cols_out(std::false_type{}, C, ldc);
+  else if (mode == 2) cols_out(std::true_type{}, C, ldc);
+  else if (mode == 3) cols_out(std::false_type{}, Ct, ldct);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,21 +598,12 @@ hipError_t launch_gemm_bf16(const GemmTask* tasks_dev, const TileRef* map_dev, i
                             int tile, hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(ntiles));
-  // ring depth: tuning knob for measurements (DMUON_GEMM_STAGES), default below
-  static const int stages_env = [] {
-    const char* v = std::getenv("DMUON_GEMM_STAGES");
-    return v ? std::atoi(v) : 0;
-  }();
+  // two 64-k stages: 128 KB of LDS at the 256 tile (one block per CU), 64 KB
+  // at the 128 tile
   if (tile == 128) {
-    if (stages_env == 8)
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 8>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 4>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 2>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
   } else if (tile == 256) {
-    if (stages_env == 4)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 4>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 5>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 2>), grid, dim3(256), 0, stream, tasks_dev, map_dev);
   } else {
     return hipErrorInvalidValue;
   }

@@ -12,6 +12,8 @@ enum : int32_t { DT_F32 = 0, DT_BF16 = 1 };
 
 // Edge of the square element tile of the elementwise kernels.
 constexpr int kEwTile = 64;
+// Extra elements per row of every NS buffer (one 128-byte line in bf16).
+constexpr int kPitchPad = 64;
 constexpr int kEwThreads = 256;
 
 // One matrix as seen by the elementwise kernels (momentum / load / update /
@@ -78,10 +80,11 @@ struct TileRef {
   uint16_t tm, tn;
 };
 
-// Number of XCDs that workgroups are dealt to round-robin, and the edge of
-// the square groups of tiles walked together inside a task.
+// Number of XCDs that workgroups are dealt to round-robin, and the shape of
+// the groups of tiles walked together inside a task (one group is about as
+// many tiles as one XCD runs at once).
 constexpr int kNumXcd = 8;
-constexpr int kTileGroup = 4;
+constexpr int kTileGroupRows = 4, kTileGroupCols = 4;
 
 // ---- launchers (each enqueues one kernel on `stream`) ----------------------
 
