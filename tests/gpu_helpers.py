@@ -43,7 +43,8 @@ def assert_bf16_close(got: np.ndarray, ref: np.ndarray, min_exact: float = 0.999
 
 
 def check_param_step(got_new: np.ndarray, w_old: np.ndarray, ref_new_unrounded: np.ndarray,
-                     param_dtype: str, ns_tol: float, ns_precision: str, what: str = "") -> float:
+                     param_dtype: str, ns_tol: float, ns_precision: str, what: str = "",
+                     elementwise: bool = True) -> float:
     """Parameter change of one step against the oracle's change.
 
     fp32 parameters: relative error of (W_new - W_old) <= ns_tol.
@@ -52,7 +53,10 @@ def check_param_step(got_new: np.ndarray, w_old: np.ndarray, ref_new_unrounded: 
     relative error is ns_tol plus that rounding's norm over the change's norm.
     With fp32 NS products the change is accurate far below a bf16 ulp, so
     additionally every element must sit within one ulp of the oracle's rounded
-    value, 99 % of them equal.  Returns the measured relative error."""
+    value, 99 % of them equal (``elementwise``; large square matrices, whose
+    near-singular directions the iteration amplifies, can hold single
+    elements beyond that even when the NS output meets its tolerance).
+    Returns the measured relative error."""
     d_ref = ref_new_unrounded - w_old
     err = rel(got_new - w_old, d_ref)
     if param_dtype == "f32":
@@ -60,7 +64,7 @@ def check_param_step(got_new: np.ndarray, w_old: np.ndarray, ref_new_unrounded: 
         return err
     allow = float(np.linalg.norm(0.5 * bf16_ulp(got_new)) / np.linalg.norm(d_ref))
     assert err <= ns_tol + allow, (what, err, allow)
-    if ns_precision == "f32":
+    if ns_precision == "f32" and elementwise:
         from oracle import muon as _orc
         # fp32 evaluation of the update, and the NS error itself, which near a
         # cancellation (W_new close to 0) can span several ulps of the result
