@@ -6,18 +6,31 @@ the 3B decoder shapes (196 matrices, 2.82 G elements, bf16 params and grads,
 fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload 2] [--ns-backend gram]
-                  [--ns-precision bf16] [--no-cpu-baseline]
+                  [--ns-precision bf16] [--no-cpu-baseline] [--copy-probe]
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR      (writes the traffic summary)
+
+HBM traffic of the GEMM kernel comes from two rocprofv3 counter runs of this
+script (FETCH_SIZE, then WRITE_SIZE, with --copy-probe so that each run also
+holds a plain 1 GiB device copy whose counter reading calibrates the
+counter): --pmc-summary turns them into TRAFFIC_SUMMARY, which later runs read
+while the GEMM source is unchanged (its SHA-256 is recorded there).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_3b_stack_hbm_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "gemm.hip")
+COPY_PROBE_BYTES = 1 << 30
 
 METRIC = "NS TFLOP/s and optimizer steps/s for a 3B-shaped owner set; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
@@ -36,7 +49,62 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="auto",
                     help="'auto' (one matrix of each distinct shape) or 'none'")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, copy 1 GiB device to device (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
     return ap.parse_args()
+
+
+def source_sha256(path=GEMM_SOURCE):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, dispatch id, value) of one counter from a rocprofv3 csv directory."""
+    out = []
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        if r["Counter_Name"] == counter:
+                            out.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return out
+
+
+def pmc_summary(fetch_dir, write_dir, steps):
+    """Per-launch HBM bytes of the GEMM kernel over the last ``steps`` steps'
+    launches, each counter scaled by its reading for the 1 GiB copy."""
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        gemm = sorted((di, v) for k, di, v in rows if "gemm_bf16_kernel" in k)
+        copies = sorted((di, v) for k, di, v in rows if "gemm" not in k and "dmuon" not in k)
+        if not gemm or not copies:
+            raise SystemExit(f"no gemm or copy dispatches in {d}")
+        copy_kib = copies[-1][1]                 # the probe is the last dispatch
+        factor = (COPY_PROBE_BYTES / 1024.0) / copy_kib
+        last = [v for _, v in gemm[-16 * steps:]]
+        res[counter] = {"kib_per_launch": sum(last) / len(last), "copy_kib": copy_kib, "factor": factor,
+                        "bytes_per_launch": sum(last) / len(last) * 1024.0 * factor, "launches": len(last)}
+    return res
+
+
+def read_traffic():
+    """Bytes per GEMM launch from the committed summary, if it was taken on
+    the current GEMM source; else None."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_val or m_sha.group(1) != source_sha256():
+        return None
+    return float(m_val.group(1))
 
 
 def nominal_flops(shapes, ns_steps):
@@ -98,6 +166,19 @@ def cpu_baseline(w, hp, budget_s=30.0):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        steps = 1
+        r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], steps)
+        tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
+        print(f"# HBM traffic of gemm_bf16_kernel, 3B 28-layer stack (workload 2), gram, bf16\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            x = r[c]
+            print(f"- {c}: {x['kib_per_launch']:.6g} KiB per launch (mean of {x['launches']} launches of one step); "
+                  f"1 GiB copy reads {x['copy_kib']:.6g} KiB -> factor {x['factor']:.4f}; "
+                  f"{x['bytes_per_launch'] / 1e9:.4f} GB per launch")
+        print(f"- hbm_bytes_per_launch: {tot:.6e}")
+        print(f"- gemm_source_sha256: {source_sha256()}")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the owner step runs on one device with no "
               f"collectives; --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -154,6 +235,13 @@ def main():
     wall = time.perf_counter() - t0
     prof = dm.dmuon_profile_end()["kernels"]
     ms_total = start.elapsed_time(end)
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step = ms_total / args.steps
     print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
           file=sys.stderr, flush=True)
@@ -165,7 +253,10 @@ def main():
     ns_ms = sum(v["ms"] for v in gemm.values()) / args.steps
     exec_flops = sum(v["flops"] for v in gemm.values()) / args.steps
     dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
+    # algorithmic flops of the step's launches over their summed duration:
+    # the duration-weighted mean over launches of flops / launch time
     achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    traffic = read_traffic()
     kernels = {k: {"launches_per_step": v["launches"] / args.steps,
                    "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
@@ -196,7 +287,10 @@ def main():
         "ns_ms_per_step": ns_ms,
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch",
+                     "launches": dom["launches"], "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
