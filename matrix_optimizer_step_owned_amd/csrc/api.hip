@@ -850,7 +850,10 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
   for (int j = 0; j < P.n; ++j) {
     const dmuon_matrix_t& m = mats[active[j]];
     const int64_t ne = m.rows * m.cols;
-    mom_bytes += ne * (int64_t(dtype_size(m.grad_dtype)) + 8 + int64_t(dtype_size(wide_dt)));
+    // gradient in, momentum in and out, the NS input out (twice when its
+    // transpose is kept as well)
+    const int64_t outs = P.mats[j].x0t != kNone ? 2 : 1;
+    mom_bytes += ne * (int64_t(dtype_size(m.grad_dtype)) + 8 + outs * int64_t(dtype_size(wide_dt)));
     upd_bytes += ne * (2 * int64_t(dtype_size(m.param_dtype)) + int64_t(dtype_size(wide_dt)));
   }
   DMUON_HIP_TRY(prof_launch(PK_MOMENTUM, 0, mom_bytes, stream, [&] {
