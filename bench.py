@@ -115,32 +115,42 @@ def nominal_flops(shapes, ns_steps):
     return tot
 
 
-def cpu_baseline(w, hp, budget_s=30.0):
+def cpu_baseline(w, hp, budget_s=30.0, min_s=10.0):
     """The oracle timed on this host: one step of one matrix of each distinct
-    shape (inputs from the seeded generator), extrapolated to the workload by
-    shape counts."""
+    shape (inputs from the seeded generator), repeated over further matrices
+    of the same shapes until at least ``min_s`` seconds are timed, then
+    extrapolated to the workload by shape counts."""
     import numpy as np
     import dmuon_inputs as di
     from oracle import muon as orc
     shapes = {}
     for i, m in enumerate(w.matrices):
         shapes.setdefault((m.rows, m.cols), []).append(i)
-    per_shape = {}
+    times = {}
     t_start = time.time()
     sampled = 0
-    for (r, c), idx in sorted(shapes.items(), key=lambda kv: kv[0][0] * kv[0][1]):
-        i = idx[0]
-        _, wexact = di.param_init(w, i)
-        _, g = di.grad_at(w, i, 0)
-        t0 = time.perf_counter()
-        orc.muon_step(wexact, g, np.zeros_like(g), lr=hp["lr"], momentum=hp["momentum"],
-                      nesterov=hp["nesterov"], ns_steps=hp["ns_steps"],
-                      weight_decay=hp["weight_decay"], ns_backend=hp["ns_backend"],
-                      param_dtype=w.param_dtype)
-        per_shape[(r, c)] = time.perf_counter() - t0
-        sampled += 1
-        if time.time() - t_start > budget_s:
+    timed = 0.0
+    for rnd in range(64):
+        for (r, c), idx in sorted(shapes.items(), key=lambda kv: kv[0][0] * kv[0][1]):
+            if rnd >= len(idx):
+                continue
+            i = idx[rnd]
+            _, wexact = di.param_init(w, i)
+            _, g = di.grad_at(w, i, 0)
+            t0 = time.perf_counter()
+            orc.muon_step(wexact, g, np.zeros_like(g), lr=hp["lr"], momentum=hp["momentum"],
+                          nesterov=hp["nesterov"], ns_steps=hp["ns_steps"],
+                          weight_decay=hp["weight_decay"], ns_backend=hp["ns_backend"],
+                          param_dtype=w.param_dtype)
+            dt = time.perf_counter() - t0
+            times.setdefault((r, c), []).append(dt)
+            timed += dt
+            sampled += 1
+            if time.time() - t_start > budget_s:
+                break
+        if timed >= min_s or time.time() - t_start > budget_s:
             break
+    per_shape = {s: sum(v) / len(v) for s, v in times.items()}
     if len(per_shape) < len(shapes):
         # extrapolate the unsampled shapes by nominal flops of the sampled ones
         rate = sum(nominal_flops([s], hp["ns_steps"]) for s in per_shape) / sum(per_shape.values())
@@ -157,10 +167,9 @@ def cpu_baseline(w, hp, budget_s=30.0):
         "value": flops / t_step / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads),
         "kind": "oracle",
         "steps_per_s": 1.0 / t_step, "matrices_per_s": len(w.matrices) / t_step,
-        "sample": (f"float64 numpy oracle, one step of one matrix of each of the "
-                   f"{len(shapes)} distinct shapes ({sampled} timed, "
-                   f"{sum(per_shape[s] for s in per_shape if s in per_shape):.1f} s), "
-                   f"extrapolated to {len(w.matrices)} matrices by shape counts"),
+        "sample": (f"float64 numpy oracle, one step each of {sampled} matrices covering "
+                   f"{len(times)} of the {len(shapes)} distinct shapes ({timed:.1f} s timed), "
+                   f"mean time per shape extrapolated to {len(w.matrices)} matrices by shape counts"),
     }
 
 
