@@ -295,55 +295,78 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Ring of kStages stages, 64 k each.  Stage kt's data sits in slot kt %
-  // kStages.  Per stage: quarters 0-2 run on fragments already in registers
-  // while the next quarter's load; then one barrier, at which stage kt+1 has
-  // landed (own loads counted, everyone's by the barrier) and every wave has
-  // finished its LDS reads of stage kt; quarter 3 then issues the loads of
-  // stage kt+kStages into stage kt's slot and the reads of stage kt+1's
-  // first quarter.  The loop is branch-free: past the last stage, loads
-  // re-fetch the last stage (in bounds, same bytes) and fragment reads
-  // re-read it, so the wait counts are constants.
+  // Ring of two stages, 64 k each; stage kt's data sits in slot kt % 2.
+  // Per stage: quarters 0-2 run on fragments already in registers while the
+  // next quarter's load; then one barrier, at which stage kt+1 has landed
+  // (own loads counted, everyone's by the barrier) and every wave has
+  // finished its LDS reads of stage kt; quarter 3 issues the reads of stage
+  // kt+1's first quarter and the first half of stage kt+2's loads into stage
+  // kt's slot, and quarter 0 of the next stage the second half, so that the
+  // loads' LDS writes spread over two quarters.  The loop is branch-free:
+  // past the last stage, loads re-fetch the last stage (in bounds, same
+  // bytes) and fragment reads re-read it, so the wait counts are constants.
+  static_assert(kStages == 2, "two-slot ring");
+  constexpr int HALF = LOADS / 2;
+  auto issue_half = [&](int data, int slot, int h) {
+    char* st = smem + (slot % kStages) * STB;
 #pragma unroll
-  for (int s = 0; s < kStages; ++s) issue_stage(s < nk ? s : nk - 1, s);
-  wait_vmcnt<LOADS * (kStages - 1)>();
+    for (int q = h * HALF; q < (h + 1) * HALF; ++q)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
+                                       (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
+  };
+  // MFMAs of one quarter with the next reads and half a stage of loads
+  // interleaved (reads first in program order: the compiler keeps LDS
+  // reads and direct-to-LDS loads in program order)
+  // (an MFMA always goes first: its wait for this quarter's fragments must
+  // not also cover a read of the next quarter issued ahead of it)
+  auto pin_quarter_with_loads = [&]() {
+    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, 8 loads
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+      }
+    } else {                             // 4 MFMAs, 4 reads, 4 loads
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+      }
+    }
+    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && HALF == 8)
+                            : (NMFMA == 4 && NFRAG == 4 && HALF == 4), "schedule");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue_half(0, 0, 0);
+  issue_half(0, 0, 1);
+  issue_half(nk > 1 ? 1 : 0, 1, 0);
+  wait_vmcnt<HALF>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    quarter(kt, 1, fa1, fb1, fa0, fb0);
+    const int next = kt + 1 < nk ? kt + 1 : nk - 1;
+    const int ahead = kt + 2 < nk ? kt + 2 : nk - 1;
+    // quarter 0, with the second half of stage kt+1's loads
+    read_frags(kt, 1, fa1, fb1);
+    issue_half(next, kt + 1, 1);
+    mfmas(fa0, fb0);
+    pin_quarter_with_loads();
     quarter(kt, 2, fa0, fb0, fa1, fb1);
     quarter(kt, 3, fa1, fb1, fa0, fb0);
-    wait_vmcnt<LOADS * (kStages - 2)>();
+    wait_vmcnt<0>();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // (the reads come first in program order: the compiler keeps LDS reads
-    // and direct-to-LDS loads in program order)
-    read_frags(kt + 1 < nk ? kt + 1 : nk - 1, 0, fa0, fb0);
-    const int ahead = kt + kStages;
-    issue_stage(ahead < nk ? ahead : nk - 1, ahead);
+    // quarter 3, with the first half of stage kt+2's loads
+    read_frags(next, 0, fa0, fb0);
+    issue_half(ahead, kt + 2, 0);
     mfmas(fa1, fb1);
-    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, 16 loads
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-      }
-    } else {                             // 4 MFMAs, 4 reads, 8 loads
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-      }
-    }
-    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && LOADS == 16)
-                            : (NMFMA == 4 && NFRAG == 4 && LOADS == 8), "schedule");
-    __builtin_amdgcn_sched_barrier(0);
+    pin_quarter_with_loads();
   }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
