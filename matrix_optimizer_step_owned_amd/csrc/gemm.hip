@@ -286,12 +286,14 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
                      const bf16x8_t (&fa)[F], const bf16x8_t (&fb)[F]) {
     read_frags(s, kq_next, na, nb);
     mfmas(fa, fb);
+    // the reads go out two per MFMA over the first NFRAG/2 MFMAs, as early
+    // as possible behind the first one
 #pragma unroll
-    for (int i = 0; i < NFRAG; ++i) {
+    for (int i = 0; i < NFRAG / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
     }
-    if (NMFMA > NFRAG) __builtin_amdgcn_sched_group_barrier(kMfma, NMFMA - NFRAG, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, NMFMA - NFRAG / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -322,15 +324,16 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   auto pin_quarter_with_loads = [&]() {
     if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, 8 loads
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
         __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
       }
+      __builtin_amdgcn_sched_group_barrier(kMfma, 4, 1);
     } else {                             // 4 MFMAs, 4 reads, 4 loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
