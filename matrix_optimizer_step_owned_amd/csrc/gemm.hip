@@ -126,6 +126,7 @@ __device__ __forceinline__ void store_fragment(const f32x16_t& a, OutT* __restri
 // ---------------------------------------------------------------------------
 
 constexpr int kStageK = 64;                     // k per LDS stage
+constexpr int kLoadsEarly256 = 8;               // of a stage's 16 loads per wave, issued a quarter early
 constexpr int kRowBytes = kStageK * 2;          // 128: one cache line per row
 constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows filled by one wave-wide DMA load
 
@@ -308,33 +309,50 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // past the last stage, loads re-fetch the last stage (in bounds, same
   // bytes) and fragment reads re-read it, so the wait counts are constants.
   static_assert(kStages == 2, "two-slot ring");
-  constexpr int HALF = LOADS / 2;
-  auto issue_half = [&](int data, int slot, int h) {
+  // loads of a stage issued in quarter 3 (the rest go in the next quarter 0)
+  constexpr int LQ3 = BT == 256 ? kLoadsEarly256 : LOADS / 2;
+  constexpr int LQ0 = LOADS - LQ3;
+  auto issue_part = [&](int data, int slot, int h) {
     char* st = smem + (slot % kStages) * STB;
 #pragma unroll
-    for (int q = h * HALF; q < (h + 1) * HALF; ++q)
+    for (int q = h ? LQ3 : 0; q < (h ? LOADS : LQ3); ++q)
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
                                        (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
   };
-  // MFMAs of one quarter with the next reads and half a stage of loads
-  // interleaved (reads first in program order: the compiler keeps LDS
-  // reads and direct-to-LDS loads in program order)
-  // (an MFMA always goes first: its wait for this quarter's fragments must
-  // not also cover a read of the next quarter issued ahead of it)
-  auto pin_quarter_with_loads = [&]() {
-    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, 8 loads
+  // MFMAs of one quarter with the next quarter's reads and part of a stage's
+  // loads interleaved; the reads come first in program order (the compiler
+  // keeps LDS reads and direct-to-LDS loads in program order) and an MFMA
+  // always goes first (its wait for this quarter's fragments must not also
+  // cover a read of the next quarter issued ahead of it)
+  auto pin_quarter_with_loads = [&](auto nloads) {
+    constexpr int V = decltype(nloads)::value;
+    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, V loads
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
         __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
       }
+      if constexpr (V > 12) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+        for (int i = 0; i < V - 12; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 24 - V; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+        }
+        if constexpr (V < 12) __builtin_amdgcn_sched_group_barrier(kMfma, 12 - V, 1);
       }
-      __builtin_amdgcn_sched_group_barrier(kMfma, 4, 1);
     } else {                             // 4 MFMAs, 4 reads, 4 loads
+      static_assert(V == 4, "schedule");
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
@@ -342,34 +360,34 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
         __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
       }
     }
-    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && HALF == 8)
-                            : (NMFMA == 4 && NFRAG == 4 && HALF == 4), "schedule");
+    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && V <= 16)
+                            : (NMFMA == 4 && NFRAG == 4), "schedule");
     __builtin_amdgcn_sched_barrier(0);
   };
-  issue_half(0, 0, 0);
-  issue_half(0, 0, 1);
-  issue_half(nk > 1 ? 1 : 0, 1, 0);
-  wait_vmcnt<HALF>();
+  issue_part(0, 0, 0);
+  issue_part(0, 0, 1);
+  issue_part(nk > 1 ? 1 : 0, 1, 0);
+  wait_vmcnt<LQ3>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
     const int next = kt + 1 < nk ? kt + 1 : nk - 1;
     const int ahead = kt + 2 < nk ? kt + 2 : nk - 1;
-    // quarter 0, with the second half of stage kt+1's loads
+    // quarter 0, with the rest of stage kt+1's loads
     read_frags(kt, 1, fa1, fb1);
-    issue_half(next, kt + 1, 1);
+    issue_part(next, kt + 1, 1);
     mfmas(fa0, fb0);
-    pin_quarter_with_loads();
+    pin_quarter_with_loads(std::integral_constant<int, LQ0>{});
     quarter(kt, 2, fa0, fb0, fa1, fb1);
     quarter(kt, 3, fa1, fb1, fa0, fb0);
     wait_vmcnt<0>();
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // quarter 3, with the first half of stage kt+2's loads
+    // quarter 3, with the first part of stage kt+2's loads
     read_frags(next, 0, fa0, fb0);
-    issue_half(ahead, kt + 2, 0);
+    issue_part(ahead, kt + 2, 0);
     mfmas(fa1, fb1);
-    pin_quarter_with_loads();
+    pin_quarter_with_loads(std::integral_constant<int, LQ3>{});
   }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
