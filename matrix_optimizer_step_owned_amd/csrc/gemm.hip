@@ -157,9 +157,6 @@ __device__ __forceinline__ u32x4_t gload_u32x4(const void* p) {
 __device__ __forceinline__ void gstore_u32x4(void* p, u32x4_t v) {
   *reinterpret_cast<GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p)) = v;
 }
-__device__ __forceinline__ void gstore_u16(void* p, uint16_t v) {
-  *reinterpret_cast<GLOBAL_AS uint16_t*>(reinterpret_cast<uintptr_t>(p)) = v;
-}
 __device__ __forceinline__ float gload_f32(const float* p) {
   return *reinterpret_cast<const GLOBAL_AS float*>(reinterpret_cast<uintptr_t>(p));
 }
@@ -473,9 +470,65 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   }
   lds_barrier();
 
+  // 8 x 4 block transposes: lane tq takes rows 8rb..8rb+7 of columns
+  // 8cc + 4hf + 0..3 of the staged tile and returns, for sc = 0..3, tile
+  // column 8cc + 4hf + sc over those 8 rows as one 16-byte piece
+  constexpr int LPC = 2 * (BT / 8);              // lanes per column chunk
+  constexpr int NTQ = BT * BT * 2 / 64 / 256;    // block transposes per thread
+  auto transpose_block = [&](int tq, int& cc, int& rb, int& hf, u32x4_t (&o)[4]) {
+    cc = tq / LPC;
+    rb = (tq % LPC) >> 1;
+    hf = tq & 1;
+    uint2 w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * rb + e;
+      w[e] = *reinterpret_cast<const uint2*>(stg + row * ROWB + ((cc ^ stg_swz(row)) << 4) + hf * 8);
+    }
+#pragma unroll
+    for (int sc = 0; sc < 4; ++sc) {
+      const uint32_t sel = (sc & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        const uint32_t lo = (sc >> 1) ? w[2 * p2].y : w[2 * p2].x;
+        const uint32_t hi = (sc >> 1) ? w[2 * p2 + 1].y : w[2 * p2 + 1].x;
+        o[sc][p2] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+    }
+  };
+
+  // A diagonal tile of a symmetric product is made exactly symmetric in
+  // LDS (every value below the diagonal replaced by its mirror above it),
+  // then leaves like any other tile, row by row, with no mirror pass.
+  if (mode == 2) {
+#pragma unroll 2
+    for (int q = 0; q < NTQ; ++q) {
+      const int tq = t + 256 * q;
+      if ((tq % LPC) >> 1 < tq / LPC) {          // row block above the column block
+        int cc, rb, hf;
+        u32x4_t o[4];
+        transpose_block(tq, cc, rb, hf, o);
+#pragma unroll
+        for (int sc = 0; sc < 4; ++sc) {
+          const int row = 8 * cc + 4 * hf + sc;  // destination: row `row`, chunk rb (below the diagonal)
+          *reinterpret_cast<u32x4_t*>(stg + row * ROWB + ((rb ^ stg_swz(row)) << 4)) = o[sc];
+        }
+      }
+    }
+    // inside the 8 x 8 blocks on the diagonal, element by element
+    for (int idx = t; idx < (BT / 8) * 64; idx += 256) {
+      const int b = idx >> 6, i = (idx >> 3) & 7, j = idx & 7;
+      if (i > j) {
+        const int r = 8 * b + i, c = 8 * b + j;  // (r, c) below, (c, r) above
+        const uint16_t v = *reinterpret_cast<const uint16_t*>(stg + c * ROWB + ((b ^ stg_swz(c)) << 4) + i * 2);
+        *reinterpret_cast<uint16_t*>(stg + r * ROWB + ((b ^ stg_swz(r)) << 4) + j * 2) = v;
+      }
+    }
+    lds_barrier();
+  }
+
   // C, row by row: thread t covers chunk t % NCH of rows t / NCH + (256 / NCH) k
-  auto rows_out = [&](auto diag_tile) {
-    constexpr bool kD = decltype(diag_tile)::value;
+  {
     constexpr int NIT = BT * NCH / 256, BATCH = 4;
     const int chunk = t % NCH;
     const int c0 = chunk * 8;
@@ -491,63 +544,28 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
         const int row = t / NCH + (256 / NCH) * (k0 + b);
-        uint16_t* const dst = cbase + int64_t(row) * ldc;
-        if (!kD || c0 >= row) {
-          gstore_u32x4(dst, v[b]);
-        } else if (c0 + 7 >= row) {              // diagonal tile: upper triangle only
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (c0 + e >= row) gstore_u16(dst + e, static_cast<uint16_t>(v[b][e >> 1] >> ((e & 1) * 16)));
-        }
+        gstore_u32x4(cbase + int64_t(row) * ldc, v[b]);
       }
     }
-  };
-  if (mode == 2) rows_out(std::true_type{});
-  else rows_out(std::false_type{});
+  }
 
-  // mirror / Ct, column by column: a lane takes rows 8rb..8rb+7 of columns
-  // 8cc + 4hf + 0..3 and writes them as rows of the destination
-  auto cols_out = [&](auto diag_tile, uint16_t* const Tdst, const int64_t ldt) {
-    constexpr bool kD = decltype(diag_tile)::value;
-    constexpr int LPC = 2 * (BT / 8);            // lanes per column chunk
+  // mirror (off-diagonal symmetric tiles) or Ct, column by column: tile
+  // column c leaves as row c of the destination
+  if (mode == 1 || mode == 3) {
+    uint16_t* const Tdst = mode == 3 ? Ct : C;
+    const int64_t ldt = mode == 3 ? ldct : ldc;
 #pragma unroll 2
-    for (int q = 0; q < BT * BT * 2 / 64 / 256; ++q) {
-      const int tq = t + 256 * q;
-      const int cc = tq / LPC;
-      const int rb = (tq % LPC) >> 1;
-      const int hf = tq & 1;
-      uint2 w[8];
+    for (int q = 0; q < NTQ; ++q) {
+      int cc, rb, hf;
+      u32x4_t o[4];
+      transpose_block(t + 256 * q, cc, rb, hf, o);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = 8 * rb + e;
-        w[e] = *reinterpret_cast<const uint2*>(stg + row * ROWB + ((cc ^ stg_swz(row)) << 4) + hf * 8);
-      }
-      const int r0 = 8 * rb;
-#pragma unroll
-      for (int sc = 0; sc < 4; ++sc) {           // destination row: tile column 8cc + 4hf + sc
+      for (int sc = 0; sc < 4; ++sc) {
         const int col = 8 * cc + 4 * hf + sc;
-        const uint32_t sel = (sc & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t o;
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) {
-          const uint32_t lo = (sc >> 1) ? w[2 * p2].y : w[2 * p2].x;
-          const uint32_t hi = (sc >> 1) ? w[2 * p2 + 1].y : w[2 * p2 + 1].x;
-          o[p2] = __builtin_amdgcn_perm(hi, lo, sel);
-        }
-        uint16_t* const dst = Tdst + (int64_t(tn) * BT + col) * ldt + int64_t(tm) * BT + r0;
-        if (!kD || r0 + 7 < col) {
-          gstore_u32x4(dst, o);
-        } else if (r0 < col) {                   // diagonal tile: strict lower triangle only
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (r0 + e < col) gstore_u16(dst + e, static_cast<uint16_t>(o[e >> 1] >> ((e & 1) * 16)));
-        }
+        gstore_u32x4(Tdst + (int64_t(tn) * BT + col) * ldt + int64_t(tm) * BT + 8 * rb, o[sc]);
       }
     }
-  };
-  if (mode == 1) cols_out(std::false_type{}, C, ldc);
-  else if (mode == 2) cols_out(std::true_type{}, C, ldc);
-  else if (mode == 3) cols_out(std::false_type{}, Ct, ldct);
+  }
 }
 
 // ---------------------------------------------------------------------------
