@@ -348,13 +348,13 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
         }
         if constexpr (V < 12) __builtin_amdgcn_sched_group_barrier(kMfma, 12 - V, 1);
       }
-    } else {                             // 4 MFMAs, 4 reads, 4 loads
-      static_assert(V == 4, "schedule");
+    } else {                             // 4 MFMAs, 4 reads, 4 or 0 loads
+      static_assert(V == 4 || V == 0, "schedule");
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
         __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
+        if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
       }
     }
     static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && V <= 16)
@@ -367,25 +367,43 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   wait_vmcnt<LQ3>();
   __builtin_amdgcn_s_barrier();
   read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int next = kt + 1 < nk ? kt + 1 : nk - 1;
-    const int ahead = kt + 2 < nk ? kt + 2 : nk - 1;
-    // quarter 0, with the rest of stage kt+1's loads
-    read_frags(kt, 1, fa1, fb1);
-    issue_part(next, kt + 1, 1);
-    mfmas(fa0, fb0);
-    pin_quarter_with_loads(std::integral_constant<int, LQ0>{});
-    quarter(kt, 2, fa0, fb0, fa1, fb1);
-    quarter(kt, 3, fa1, fb1, fa0, fb0);
-    wait_vmcnt<0>();
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // quarter 3, with the first part of stage kt+2's loads
-    read_frags(next, 0, fa0, fb0);
-    issue_part(ahead, kt + 2, 0);
-    mfmas(fa1, fb1);
-    pin_quarter_with_loads(std::integral_constant<int, LQ3>{});
-  }
+  // One stage.  kLast: the last stage (no loads, no reads of a next stage,
+  // no barrier); kNoAhead: the stage before it (no stage kt+2 to load).
+  auto stage_step = [&](int kt, auto last, auto no_ahead) {
+    constexpr bool kLast = decltype(last)::value, kNoAhead = decltype(no_ahead)::value;
+    if constexpr (kLast) {
+      quarter(kt, 1, fa1, fb1, fa0, fb0);
+      quarter(kt, 2, fa0, fb0, fa1, fb1);
+      quarter(kt, 3, fa1, fb1, fa0, fb0);
+      mfmas(fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // quarter 0, with the rest of stage kt+1's loads
+      read_frags(kt, 1, fa1, fb1);
+      issue_part(kt + 1, kt + 1, 1);
+      mfmas(fa0, fb0);
+      pin_quarter_with_loads(std::integral_constant<int, LQ0>{});
+      quarter(kt, 2, fa0, fb0, fa1, fb1);
+      quarter(kt, 3, fa1, fb1, fa0, fb0);
+      wait_vmcnt<0>();
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // quarter 3, with the first part of stage kt+2's loads
+      read_frags(kt + 1, 0, fa0, fb0);
+      if constexpr (kNoAhead) {
+        mfmas(fa1, fb1);
+        pin_quarter_with_loads(std::integral_constant<int, 0>{});
+      } else {
+        issue_part(kt + 2, kt + 2, 0);
+        mfmas(fa1, fb1);
+        pin_quarter_with_loads(std::integral_constant<int, LQ3>{});
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) stage_step(kt, std::false_type{}, std::false_type{});
+  if (kt + 1 < nk) stage_step(kt++, std::false_type{}, std::true_type{});
+  stage_step(kt, std::true_type{}, std::false_type{});
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
 
