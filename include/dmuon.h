@@ -169,6 +169,43 @@ int dmuon_apply_update(const dmuon_matrix_t* mats, int32_t n, const void* const*
                        int32_t update_dtype, const dmuon_hparams_t* hp, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * Gradient clipping by the global p-norm (Training Guide, "Gradient
+ * Clipping": the dedicated gradients are clipped after their reduce and
+ * before momentum and Newton-Schulz, by default with global p-norm clipping;
+ * "Fused CUDA clip for regular / Muon / AdamW": several gradient groups are
+ * clipped in one pass, each with its own norm and coefficient).  Every
+ * gradient belongs to one bucket; per bucket b:
+ *   total_b = (sum over its gradients of sum |g|^p)^(1/p)   (p = +inf: max |g|)
+ *   coef_b  = min(1, max_norm[b] / (total_b + 1e-6))
+ *   each of its gradients *= coef_b in place (fp64 product, rounded once,
+ *   to nearest-even, to the gradient's dtype); a bucket whose coefficient
+ *   is exactly 1 is not written.
+ * These are the semantics of PyTorch's clip_grad_norm_, which the same page
+ * uses for the other parameters; the norm is accumulated in fp64.  A NaN or
+ * Inf makes its bucket's total and coefficient non-finite and propagates
+ * into that bucket's gradients only (no error).
+ *   grads      host array of n descriptors (n >= 0); each grad is device
+ *              memory of numel values, contiguous, any alignment
+ *   max_norm   host array of nbuckets finite values >= 0
+ *   norm_type  p > 0, or +inf
+ *   total_norm device array of nbuckets doubles receiving total_b, or NULL
+ *   workspace  device, >= dmuon_clip_workspace_size bytes, 256-byte aligned
+ * Gradients must not overlap each other, the workspace or total_norm.
+ * n == 0 does nothing (total_norm is not written).
+ */
+typedef struct {
+  int64_t numel;    /* elements, > 0 */
+  void* grad;       /* device, numel values of `dtype`, clipped in place */
+  int32_t dtype;    /* DMUON_F32 or DMUON_BF16 */
+  int32_t bucket;   /* 0 <= bucket < nbuckets */
+} dmuon_grad_t;
+
+size_t dmuon_clip_workspace_size(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets);
+int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
+                         const double* max_norm, double norm_type, double* total_norm,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Readable name of a status code (static storage). */
 const char* dmuon_status_string(int status);
 

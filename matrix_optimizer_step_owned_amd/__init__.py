@@ -59,6 +59,11 @@ class dmuon_hparams_t(ctypes.Structure):
                 ("ns_coeffs_len", ctypes.c_int32), ("eps", ctypes.c_double)]
 
 
+class dmuon_grad_t(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("grad", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32), ("bucket", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _I64P = ctypes.POINTER(ctypes.c_int64)
@@ -78,6 +83,11 @@ EXPORTS = {
     "dmuon_apply_update_workspace_size": (ctypes.c_size_t, [ctypes.c_int32]),
     "dmuon_apply_update": (ctypes.c_int, [_MP, ctypes.c_int32, _PP, ctypes.c_int32, _HP, _P,
                                           ctypes.c_size_t, _P]),
+    "dmuon_clip_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32,
+                                                     ctypes.c_int32]),
+    "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P,
+                                            ctypes.c_size_t, _P]),
     "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dmuon_last_error": (ctypes.c_char_p, []),
     "dmuon_backend_info": (ctypes.c_char_p, []),
@@ -313,6 +323,45 @@ def dmuon_apply_update(params: List[torch.Tensor], updates: List[torch.Tensor], 
     _check(_lib.dmuon_apply_update(mats, n, _ptrs(updates), dt, ctypes.byref(h),
                                    ws.data_ptr() if ws is not None else None, wsb,
                                    _stream(stream, params[0].device)), "dmuon_apply_update")
+
+
+def dmuon_clip_grad_norm(grads: List[torch.Tensor], max_norm, *, norm_type: float = 2.0,
+                         buckets: Optional[Sequence[int]] = None, total_norm: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Clip gradients in place by their global p-norm, per bucket (every
+    gradient in bucket 0 unless ``buckets`` is given; ``max_norm`` a number or
+    one per bucket).  Returns the per-bucket totals (float64, on the device)."""
+    n = len(grads)
+    if buckets is None:
+        buckets = [0] * n
+    if len(buckets) != n:
+        raise ValueError("buckets must have one entry per gradient")
+    nb = (max(buckets) + 1) if n else 1
+    if isinstance(max_norm, (int, float)):
+        max_norm = [float(max_norm)] * nb
+    nb = max(nb, len(max_norm))
+    if len(max_norm) != nb:
+        raise ValueError("max_norm must have one value per bucket")
+    arr = (dmuon_grad_t * max(n, 1))()
+    for i, g in enumerate(grads):
+        if not g.is_contiguous():
+            raise ValueError(f"grads[{i}] must be contiguous")
+        arr[i].numel = g.numel()
+        arr[i].grad = g.data_ptr()
+        arr[i].dtype = _dtype(g)
+        arr[i].bucket = int(buckets[i])
+    if n == 0:
+        return torch.zeros(nb, dtype=torch.float64)
+    device = grads[0].device
+    if total_norm is None:
+        total_norm = torch.empty(nb, dtype=torch.float64, device=device)
+    mx = (ctypes.c_double * nb)(*[float(v) for v in max_norm])
+    nbytes = int(_lib.dmuon_clip_workspace_size(arr, n, nb)) if n else 0
+    ws, wsb = _workspace(nbytes, device, workspace)
+    _check(_lib.dmuon_clip_grad_norm(arr, n, nb, mx, float(norm_type), total_norm.data_ptr(),
+                                     ws.data_ptr() if ws is not None else None, wsb, _stream(stream, device)),
+           "dmuon_clip_grad_norm")
+    return total_norm
 
 
 def dmuon_plan_describe(shapes: Sequence[Sequence[int]], **hp) -> dict:

@@ -582,8 +582,10 @@ int check_device() {
 // measurement hooks
 // ---------------------------------------------------------------------------
 
-enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_BF16, PK_GEMM_F32, PK_UPDATE, PK_COUNT };
-const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_bf16", "gemm_f32", "update"};
+enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_BF16, PK_GEMM_F32, PK_UPDATE,
+                PK_CLIP_NORM, PK_CLIP_FINALIZE, PK_CLIP_SCALE, PK_COUNT };
+const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_bf16", "gemm_f32", "update",
+                                          "clip_norm", "clip_finalize", "clip_scale"};
 
 struct ProfRec {
   int kind;
@@ -1071,6 +1073,123 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
 }
 
 // ---- dmuon_apply_update -----------------------------------------------------
+
+// ---------------------------------------------------------------------------
+// gradient clipping
+// ---------------------------------------------------------------------------
+
+namespace {
+struct ClipLayout {
+  size_t off_items, off_bucket_blocks, off_max_norm, off_partials, off_coefs, total;
+  int64_t blocks;
+};
+
+ClipLayout clip_layout(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets) {
+  ClipLayout L{};
+  L.blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t bytes = grads[i].numel * int64_t(dtype_size(grads[i].dtype));
+    L.blocks += (bytes + kClipChunkBytes - 1) / kClipChunkBytes;
+  }
+  size_t cur = 0;
+  L.off_items = cur; cur = align_up(cur + sizeof(ClipItem) * size_t(n));
+  L.off_bucket_blocks = cur; cur = align_up(cur + sizeof(int64_t) * size_t(nbuckets + 1));
+  L.off_max_norm = cur; cur = align_up(cur + sizeof(double) * size_t(nbuckets));
+  L.off_partials = cur; cur = align_up(cur + sizeof(double) * size_t(L.blocks));
+  L.off_coefs = cur; cur = align_up(cur + sizeof(double) * size_t(nbuckets));
+  L.total = cur;
+  return L;
+}
+}  // namespace
+
+size_t dmuon_clip_workspace_size(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets) {
+  if (n <= 0 || nbuckets <= 0 || !grads) return 0;
+  for (int i = 0; i < n; ++i)
+    if (grads[i].numel <= 0 || !dtype_ok(grads[i].dtype)) return 0;
+  return clip_layout(grads, n, nbuckets).total;
+}
+
+int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                         double norm_type, double* total_norm, void* workspace, size_t workspace_bytes,
+                         void* stream_) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (nbuckets <= 0) return fail(DMUON_ERR_INVALID_ARG, "nbuckets must be >= 1");
+  if (n > 0 && !grads) return fail(DMUON_ERR_INVALID_ARG, "grads is NULL");
+  if (!max_norm) return fail(DMUON_ERR_INVALID_ARG, "max_norm is NULL");
+  if (!(norm_type > 0.0)) return fail(DMUON_ERR_INVALID_ARG, "norm_type must be > 0 (or +inf)");
+  for (int b = 0; b < nbuckets; ++b)
+    if (!std::isfinite(max_norm[b]) || max_norm[b] < 0.0)
+      return fail(DMUON_ERR_INVALID_ARG, "max_norm[" + std::to_string(b) + "] must be finite and >= 0");
+  std::vector<Range> ranges;
+  for (int i = 0; i < n; ++i) {
+    const dmuon_grad_t& g = grads[i];
+    if (!g.grad) return fail(DMUON_ERR_INVALID_ARG, mat_name("grads", i) + ".grad is NULL");
+    if (g.numel <= 0) return fail(DMUON_ERR_INVALID_ARG, mat_name("grads", i) + ".numel must be > 0");
+    if (!dtype_ok(g.dtype)) return fail(DMUON_ERR_UNSUPPORTED, mat_name("grads", i) + ".dtype must be F32 or BF16");
+    if (g.bucket < 0 || g.bucket >= nbuckets)
+      return fail(DMUON_ERR_INVALID_ARG, mat_name("grads", i) + ".bucket out of range");
+    const uintptr_t p = reinterpret_cast<uintptr_t>(g.grad);
+    ranges.push_back({p, p + size_t(g.numel) * dtype_size(g.dtype), mat_name("grads", i)});
+  }
+  if (n == 0) return DMUON_OK;
+  const ClipLayout L = clip_layout(grads, n, nbuckets);
+  if (!workspace || workspace_bytes < L.total) return fail(DMUON_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  ranges.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + L.total,
+                    "workspace"});
+  if (total_norm)
+    ranges.push_back({reinterpret_cast<uintptr_t>(total_norm),
+                      reinterpret_cast<uintptr_t>(total_norm) + sizeof(double) * size_t(nbuckets), "total_norm"});
+  int st = check_overlaps(ranges);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  // gradients ordered by bucket (stable), so each bucket's blocks are contiguous
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return grads[a].bucket < grads[b].bucket; });
+  st = stage_table(ws, L.off_partials, stream, [&](char* host) {
+    ClipItem* items = reinterpret_cast<ClipItem*>(host + L.off_items);
+    int64_t* bb = reinterpret_cast<int64_t*>(host + L.off_bucket_blocks);
+    double* mx = reinterpret_cast<double*>(host + L.off_max_norm);
+    int64_t blk = 0;
+    int k = 0;
+    for (int b = 0; b <= nbuckets; ++b) {
+      while (k < n && grads[order[k]].bucket < b) {
+        const dmuon_grad_t& g = grads[order[k]];
+        ClipItem& it = items[k];
+        it.grad = g.grad; it.numel = g.numel; it.blk_first = blk; it.dtype = g.dtype; it.bucket = g.bucket;
+        it.aligned = aligned16(g.grad);
+        blk += (g.numel * int64_t(dtype_size(g.dtype)) + kClipChunkBytes - 1) / kClipChunkBytes;
+        ++k;
+      }
+      bb[b] = blk;
+    }
+    for (int b = 0; b < nbuckets; ++b) mx[b] = max_norm[b];
+  });
+  if (st) return st;
+  const ClipItem* items_dev = reinterpret_cast<const ClipItem*>(ws + L.off_items);
+  double* partials = reinterpret_cast<double*>(ws + L.off_partials);
+  double* coefs = reinterpret_cast<double*>(ws + L.off_coefs);
+  int64_t bytes = 0;
+  for (int i = 0; i < n; ++i) bytes += grads[i].numel * int64_t(dtype_size(grads[i].dtype));
+  DMUON_HIP_TRY(prof_launch(PK_CLIP_NORM, 0, bytes, stream, [&] {
+    return launch_clip_norm(items_dev, n, L.blocks, norm_type, partials, stream);
+  }));
+  DMUON_HIP_TRY(prof_launch(PK_CLIP_FINALIZE, 0, L.blocks * 8, stream, [&] {
+    return launch_clip_finalize(reinterpret_cast<const int64_t*>(ws + L.off_bucket_blocks), nbuckets,
+                                reinterpret_cast<const double*>(ws + L.off_max_norm), partials, norm_type,
+                                total_norm, coefs, stream);
+  }));
+  DMUON_HIP_TRY(prof_launch(PK_CLIP_SCALE, 0, 2 * bytes, stream, [&] {
+    return launch_clip_scale(items_dev, n, L.blocks, coefs, stream);
+  }));
+  return DMUON_OK;
+}
 
 size_t dmuon_apply_update_workspace_size(int32_t n) {
   return n <= 0 ? 0 : align_up(sizeof(EwMat) * n);

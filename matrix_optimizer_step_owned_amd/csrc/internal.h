@@ -86,6 +86,20 @@ struct TileRef {
 constexpr int kNumXcd = 8;
 constexpr int kTileGroupRows = 4, kTileGroupCols = 4;
 
+// One gradient of a clipping call.  The host orders the items by bucket, so
+// each bucket's blocks form one contiguous range.
+struct ClipItem {
+  void* grad;          // in place
+  int64_t numel;
+  int64_t blk_first;   // first block of this gradient
+  int32_t dtype;       // DT_F32 or DT_BF16
+  int32_t bucket;
+  int32_t aligned;     // grad is 16-byte aligned
+  int32_t pad_;
+};
+constexpr int kClipThreads = 256;
+constexpr int kClipChunkBytes = 32768;   // bytes of one gradient per block
+
 // ---- launchers (each enqueues one kernel on `stream`) ----------------------
 
 // U = momentum / Nesterov (mode 0) or plain copy (mode 1) of every matrix into
@@ -107,6 +121,17 @@ hipError_t launch_gemm_bf16(const GemmTask* tasks_dev, const TileRef* map_dev, i
                             int tile, hipStream_t stream);
 hipError_t launch_gemm_f32(const GemmTask* tasks_dev, const TileRef* map_dev, int64_t ntiles,
                            int tile, hipStream_t stream);
+
+// Gradient clipping: partials[b] = sum |g|^p (max |g| for p = inf) over
+// block b; per bucket, total = the p-norm of its blocks' partials and
+// coef = min(1, max_norm / (total + 1e-6)); then every gradient *= coef.
+hipError_t launch_clip_norm(const ClipItem* items_dev, int n, int64_t nblocks, double p, double* partials,
+                            hipStream_t stream);
+hipError_t launch_clip_finalize(const int64_t* bucket_blocks_dev, int nbuckets, const double* max_norm_dev,
+                                const double* partials, double p, double* total_out, double* coefs,
+                                hipStream_t stream);
+hipError_t launch_clip_scale(const ClipItem* items_dev, int n, int64_t nblocks, const double* coefs,
+                             hipStream_t stream);
 
 // Tile edges of the grouped GEMM kernels.
 constexpr int kTileBf16 = 128;

@@ -200,3 +200,44 @@ def test_tile_maps_cover_every_tile_once(dm):
     # the element count must fit the 16-bit tile coordinates
     with pytest.raises(dm.DmuonError):
         dm.dmuon_plan_describe([(1 << 23, 16)])
+
+
+def test_clip_argument_errors_before_launch(dm):
+    """Every clipping argument check runs before anything touches a device
+    (fake device addresses are never dereferenced)."""
+    lib = dm._lib
+
+    def grads(specs):
+        arr = (dm.dmuon_grad_t * len(specs))()
+        base = 1 << 41
+        for i, (numel, dt, bucket) in enumerate(specs):
+            arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = numel, base + i * (1 << 30), dt, bucket
+        return arr
+
+    def call(g, n, nb=2, mx=(1.0, 1.0), p=2.0, ws=1 << 40, wsb=1 << 40):
+        m = (ctypes.c_double * len(mx))(*mx)
+        return lib.dmuon_clip_grad_norm(g, n, nb, m, p, None, ws, wsb, None)
+
+    ok = grads([(1000, dm.DMUON_BF16, 0), (77, dm.DMUON_F32, 1)])
+    need = lib.dmuon_clip_workspace_size(ok, 2, 2)
+    # one 32 KB chunk per gradient here: 2 blocks of fp64 partials plus the tables
+    assert 2 * 8 < need < 4096
+    assert call(ok, -1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 2, nb=0) == dm.DMUON_ERR_INVALID_ARG
+    assert call(grads([(1000, dm.DMUON_BF16, 2)]), 1) == dm.DMUON_ERR_INVALID_ARG       # bucket out of range
+    assert call(grads([(0, dm.DMUON_BF16, 0)]), 1) == dm.DMUON_ERR_INVALID_ARG          # empty gradient
+    assert call(grads([(10, 5, 0)]), 1) == dm.DMUON_ERR_UNSUPPORTED                     # dtype
+    assert call(ok, 2, mx=(1.0, -1.0)) == dm.DMUON_ERR_INVALID_ARG                      # max_norm < 0
+    assert call(ok, 2, mx=(float("nan"), 1.0)) == dm.DMUON_ERR_INVALID_ARG
+    for p in (0.0, -2.0, float("nan")):
+        assert call(ok, 2, p=p) == dm.DMUON_ERR_INVALID_ARG, p
+    nul = grads([(1000, dm.DMUON_BF16, 0)])
+    nul[0].grad = None
+    assert call(nul, 1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 2, ws=None) == dm.DMUON_ERR_WORKSPACE
+    assert call(ok, 2, wsb=need - 1) == dm.DMUON_ERR_WORKSPACE
+    assert call(ok, 2, ws=(1 << 40) + 8, wsb=need) == dm.DMUON_ERR_INVALID_ARG          # misaligned
+    dup = grads([(1000, dm.DMUON_BF16, 0), (1000, dm.DMUON_BF16, 1)])
+    dup[1].grad = dup[0].grad + 100
+    assert call(dup, 2) == dm.DMUON_ERR_ALIASING
+    assert call(ok, 0, ws=None, wsb=0) == dm.DMUON_OK                                    # nothing to do
