@@ -8,6 +8,12 @@ fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--workload 2] [--ns-backend gram]
                   [--ns-precision bf16] [--no-cpu-baseline] [--copy-probe]
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR      (writes the traffic summary)
+  python bench.py --clip [--steps K] [--warmup W]        (gradient clipping alone)
+  python bench.py --clip --pmc-summary FETCH_DIR WRITE_DIR
+
+--clip times dmuon_clip_grad_norm over the same gradient set (one bucket,
+p = 2, clipping active on every call: each call's max_norm is half the
+gradients' current norm) and prints its own JSON line, HBM-bound.
 
 HBM traffic of the GEMM kernel comes from two rocprofv3 counter runs of this
 script (FETCH_SIZE, then WRITE_SIZE, with --copy-probe so that each run also
@@ -30,6 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_3b_stack_hbm_traffic.md")
 GEMM_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "gemm.hip")
+CLIP_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "clip_scale_3b_stack_grads_hbm_traffic.md")
+CLIP_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "clip.hip")
+CLIP_METRIC = "gradient clipping GB/s (per-bucket global 2-norm clip, in place) for a 3B-shaped gradient set"
 COPY_PROBE_BYTES = 1 << 30
 
 METRIC = "NS TFLOP/s and optimizer steps/s for a 3B-shaped owner set; % bf16 MFMA peak"
@@ -53,6 +62,8 @@ def parse():
                     help="after the timed steps, copy 1 GiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
+    ap.add_argument("--clip", action="store_true",
+                    help="time gradient clipping of the workload's gradients instead of the step")
     return ap.parse_args()
 
 
@@ -74,35 +85,36 @@ def _pmc_rows(d, counter):
     return out
 
 
-def pmc_summary(fetch_dir, write_dir, steps):
-    """Per-launch HBM bytes of the GEMM kernel over the last ``steps`` steps'
-    launches, each counter scaled by its reading for the 1 GiB copy."""
+def pmc_summary(fetch_dir, write_dir, steps, kernel="gemm_bf16_kernel", per_step=16):
+    """Per-launch HBM bytes of one kernel over the last ``steps`` steps'
+    launches (``per_step`` each), each counter scaled by its reading for the
+    1 GiB copy."""
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _pmc_rows(d, counter)
-        gemm = sorted((di, v) for k, di, v in rows if "gemm_bf16_kernel" in k)
-        copies = sorted((di, v) for k, di, v in rows if "gemm" not in k and "dmuon" not in k)
+        gemm = sorted((di, v) for k, di, v in rows if kernel in k)
+        copies = sorted((di, v) for k, di, v in rows if "dmuon" not in k)
         if not gemm or not copies:
-            raise SystemExit(f"no gemm or copy dispatches in {d}")
+            raise SystemExit(f"no {kernel} or copy dispatches in {d}")
         copy_kib = copies[-1][1]                 # the probe is the last dispatch
         factor = (COPY_PROBE_BYTES / 1024.0) / copy_kib
-        last = [v for _, v in gemm[-16 * steps:]]
+        last = [v for _, v in gemm[-per_step * steps:]]
         res[counter] = {"kib_per_launch": sum(last) / len(last), "copy_kib": copy_kib, "factor": factor,
                         "bytes_per_launch": sum(last) / len(last) * 1024.0 * factor, "launches": len(last)}
     return res
 
 
-def read_traffic():
-    """Bytes per GEMM launch from the committed summary, if it was taken on
-    the current GEMM source; else None."""
+def read_traffic(summary=TRAFFIC_SUMMARY, source=GEMM_SOURCE):
+    """Bytes per launch of the summarised kernel from the committed summary,
+    if it was taken on the current source of that kernel; else None."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(summary) as f:
             text = f.read()
     except OSError:
         return None
-    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_val or m_sha.group(1) != source_sha256():
+    if not m_sha or not m_val or m_sha.group(1) != source_sha256(source):
         return None
     return float(m_val.group(1))
 
@@ -175,6 +187,18 @@ def cpu_baseline(w, hp, budget_s=30.0, min_s=10.0):
 
 def main():
     args = parse()
+    if args.pmc_summary and args.clip:
+        r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], 1, kernel="clip_scale_kernel", per_step=1)
+        tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
+        print(f"# HBM traffic of clip_scale_kernel, gradients of the 3B 28-layer stack (bf16), p = 2\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            x = r[c]
+            print(f"- {c}: {x['kib_per_launch']:.6g} KiB per launch (the last timed call); "
+                  f"1 GiB copy reads {x['copy_kib']:.6g} KiB -> factor {x['factor']:.4f}; "
+                  f"{x['bytes_per_launch'] / 1e9:.4f} GB per launch")
+        print(f"- hbm_bytes_per_launch: {tot:.6e}")
+        print(f"- clip_source_sha256: {source_sha256(CLIP_SOURCE)}")
+        return
     if args.pmc_summary:
         steps = 1
         r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], steps)
@@ -197,6 +221,8 @@ def main():
     import matrix_optimizer_step_owned_amd as dm
 
     dev = torch.device("cuda:0")
+    if args.clip:
+        return run_clip(args, dev)
     w = di.workload(args.workload)
     hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
     shapes = [(m.rows, m.cols) for m in w.matrices]
@@ -245,12 +271,7 @@ def main():
     prof = dm.dmuon_profile_end()["kernels"]
     ms_total = start.elapsed_time(end)
     if args.copy_probe:
-        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
     ms_step = ms_total / args.steps
     print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
           file=sys.stderr, flush=True)
@@ -304,6 +325,121 @@ def main():
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, hp)
+    print(json.dumps(out), flush=True)
+
+
+def copy_probe(dev):
+    """A plain 1 GiB device-to-device copy (calibrates the HBM byte counters)."""
+    import torch
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def clip_cpu_baseline(w, budget_s=60.0, min_s=10.0):
+    """The clipping oracle timed on this host over whole gradients of the
+    workload (seeded, bf16-valued; one drawn per distinct shape and reused for
+    the other matrices of that shape), one bucket per call, in the workload's
+    order until ``min_s`` seconds are timed; reported as gradient bytes (bf16)
+    per second."""
+    import dmuon_inputs as di
+    from oracle import clip as orc_clip
+    t_start = time.time()
+    timed, nbytes, done = 0.0, 0, 0
+    by_shape = {}
+    for i, m in enumerate(w.matrices):
+        if (m.rows, m.cols) not in by_shape:
+            by_shape[(m.rows, m.cols)] = di.grad_at(w, i, 0)[1]
+        g = by_shape[(m.rows, m.cols)]
+        t0 = time.perf_counter()
+        _, tot, _ = orc_clip.clip_grad_norm([g], [0], [1e-4], 2.0)
+        timed += time.perf_counter() - t0
+        nbytes += g.size * 2
+        done += 1
+        if timed >= min_s or time.time() - t_start > budget_s:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": nbytes / timed / 1e9, "unit": "GB/s of bf16 gradient clipped", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle, norm and scale of the first {done} gradients of the "
+                       f"workload, one call each ({nbytes / 1e9:.3f} GB as bf16, {timed:.1f} s timed)")}
+
+
+def run_clip(args, dev):
+    """Gradient clipping alone: dmuon_clip_grad_norm over the workload's
+    gradient set; a step is one call (norm, finalize, scale)."""
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+
+    w = di.workload(args.workload)
+    gdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
+    esize = 2 if w.grad_dtype == "bf16" else 4
+    grads = []
+    for i, m in enumerate(w.matrices):
+        t = torch.empty(m.rows, m.cols, dtype=gdt, device=dev)
+        di.torch_normal_(t, w.grad_std, seed=100000 + i)
+        grads.append(t)
+    nbytes = w.numel * esize
+    total = torch.empty(1, dtype=torch.float64, device=dev)
+    # the current norm (nothing clipped: max_norm far above it)
+    dm.dmuon_clip_grad_norm(grads, 1e30, total_norm=total)
+    norm = float(total.cpu()[0])
+    stream = torch.cuda.current_stream(dev)
+    print(f"# clip of {len(grads)} gradients, {nbytes / 1e9:.3f} GB, norm {norm:.6g}", file=sys.stderr, flush=True)
+    # each call halves the norm: the coefficient is about 0.5 on every call
+    for s in range(args.warmup):
+        norm *= 0.5
+        dm.dmuon_clip_grad_norm(grads, norm, total_norm=total)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    dm.dmuon_profile_begin()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        norm *= 0.5
+        dm.dmuon_clip_grad_norm(grads, norm, total_norm=total)
+    end.record(stream)
+    torch.cuda.synchronize()
+    prof = dm.dmuon_profile_end()["kernels"]
+    ms_step = start.elapsed_time(end) / args.steps
+    if args.copy_probe:
+        copy_probe(dev)
+    # every call wrote: the scale kernel ran on every gradient
+    alg_bytes = 3 * nbytes
+    value = alg_bytes / (ms_step * 1e-3) / 1e9
+    dom = prof["clip_scale"]
+    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    kernels = {k: {"launches_per_step": v["launches"] / args.steps, "ms_per_step": v["ms"] / args.steps,
+                   "gbs": v["bytes"] / (v["ms"] * 1e-3) / 1e9}
+               for k, v in prof.items()}
+    out = {
+        "metric": CLIP_METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64 accumulation, " + w.grad_dtype + " gradients",
+        "data": "synthetic (seeded normal gradients, generated on device)",
+        "config": {"workload": w.name + " gradients", "tensors": len(grads), "elements": w.numel,
+                   "grad_dtype": w.grad_dtype, "norm_type": 2, "buckets": 1,
+                   "alg_bytes_per_call": alg_bytes},
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": "clip_scale", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": read_traffic(CLIP_TRAFFIC_SUMMARY, CLIP_SOURCE),
+                     "traffic_unit": "HBM bytes per launch", "launches": dom["launches"],
+                     "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = clip_cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
 

@@ -98,7 +98,8 @@ struct ClipItem {
   int32_t pad_;
 };
 constexpr int kClipThreads = 256;
-constexpr int kClipChunkBytes = 32768;   // bytes of one gradient per block
+constexpr int kClipFinalizeThreads = 1024;
+constexpr int kClipChunkBytes = 65536;   // bytes of one gradient per block
 
 // ---- launchers (each enqueues one kernel on `stream`) ----------------------
 

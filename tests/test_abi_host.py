@@ -220,7 +220,7 @@ def test_clip_argument_errors_before_launch(dm):
 
     ok = grads([(1000, dm.DMUON_BF16, 0), (77, dm.DMUON_F32, 1)])
     need = lib.dmuon_clip_workspace_size(ok, 2, 2)
-    # one 32 KB chunk per gradient here: 2 blocks of fp64 partials plus the tables
+    # one 64 KB chunk per gradient here: 2 blocks of fp64 partials plus the tables
     assert 2 * 8 < need < 4096
     assert call(ok, -1) == dm.DMUON_ERR_INVALID_ARG
     assert call(ok, 2, nb=0) == dm.DMUON_ERR_INVALID_ARG

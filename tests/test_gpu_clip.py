@@ -20,7 +20,10 @@ from tests.gpu_helpers import DEV, assert_bf16_close, f64, upload
 
 pytestmark = pytest.mark.gpu
 
-SIZES = [(1000,), (33, 7), (16384,), (16385,), (3, 70000), (8192 + 3,), (5,), (130, 257)]
+# bf16 at even, f32 at odd positions; a block takes 64 KB of one gradient:
+# whole chunks, one chunk plus a few elements, and sizes below one chunk
+SIZES = [(1000,), (33, 7), (16384,), (16385,), (3, 70000), (8192 + 3,), (5,), (130, 257),
+         (32768,), (16384,), (32769,)]
 
 
 def _grads(seed, dtypes, scales):
