@@ -157,6 +157,56 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Newton-Schulz of matrices held as tensor-parallel shards (FAQ, "Does DMuon
+ * work with Tensor Parallelism?": the Gram Newton-Schulz iteration of a TP
+ * sharded matrix exchanges only Gram matrices, by all-reduce, whose size is
+ * the square of the unsplit dimension).  On one device this runs every
+ * shard's part of that scheme; the sum of the per-shard partial Gram
+ * matrices stands in for the all-reduce.
+ * Matrix i is mats[i].nshards contiguous blocks of one logical matrix U,
+ * split along one dimension:
+ *   split = 1: column blocks; every shard has the same rows d, U = [U_0 | U_1 | ...]
+ *   split = 0: row blocks; every shard has the same cols d, U = [U_0; U_1; ...]
+ * With X_i the shard with d as its rows (U_i, or U_i^T for row blocks) and
+ * D the sum of the shards' other dimension:
+ *   X0_i = X_i / (||U||_F + eps)       (||U||_F over all shards)
+ *   Gram form (backend "gram" and D >= 2d): R = sum_i X0_i X0_i^T, the d x d
+ *     iteration of dmuon_orthogonalize's Gram form, O_i = Q X0_i;
+ *   direct form (otherwise): every iteration A = sum_i X_i X_i^T,
+ *     B = bA + cA^2, X_i <- a X_i + B X_i;
+ * and O_i is written to shards[s].out in the shard's stored orientation.
+ * The result equals dmuon_orthogonalize of the joined matrix up to rounding
+ * (the Gram sum adds the shards' rounded partial products).  d > D (a Gram
+ * matrix over the longer side) is allowed and takes the direct form, at
+ * the higher cost of its d x d products.  Shards of one matrix share the
+ * d x d work; each shard's products run at its own size.
+ *   mats       host array of n descriptors (n >= 0)
+ *   shards     host array of nshards descriptors per matrix, in order along
+ *              the split; in/out device, rows x cols row-major of io_dtype;
+ *              out may equal in, outputs must not overlap anything else
+ * Uses hp->ns_steps, ns_backend, ns_precision, ns_coeffs and eps.  n == 0
+ * does nothing.  Errors as for dmuon_orthogonalize, plus INVALID_ARG for
+ * nshards < 1, a split other than 0 or 1, or shards whose d differ.
+ */
+typedef struct {
+  int64_t rows, cols;   /* this shard as stored, > 0 */
+  const void* in;       /* device, rows*cols values of io_dtype */
+  void* out;            /* device, rows*cols values of io_dtype; may equal in */
+} dmuon_shard_t;
+
+typedef struct {
+  const dmuon_shard_t* shards;   /* host array of nshards */
+  int32_t nshards;               /* >= 1 */
+  int32_t split;                 /* 1: column blocks, 0: row blocks */
+} dmuon_sharded_t;
+
+size_t dmuon_orthogonalize_sharded_workspace_size(const dmuon_sharded_t* mats, int32_t n,
+                                                  const dmuon_hparams_t* hp);
+int dmuon_orthogonalize_sharded(const dmuon_sharded_t* mats, int32_t n, int32_t io_dtype,
+                                const dmuon_hparams_t* hp, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * The update stage alone: W <- W*(1 - lr*weight_decay) -
  * lr*0.2*sqrt(max(rows,cols))*O for every matrix (Hyperparameter Guide, lr
  * row; weight_decay of Step 4), with O = update[i] (device, rows x cols as

@@ -12,7 +12,7 @@ from __future__ import annotations
 import ctypes
 import json
 import os
-from typing import List, Optional, Sequence
+from typing import List, Optional, Sequence, Tuple
 
 import torch  # loaded first so that the library binds to torch's HIP runtime
 
@@ -64,6 +64,16 @@ class dmuon_grad_t(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("bucket", ctypes.c_int32)]
 
 
+class dmuon_shard_t(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("in_", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class dmuon_sharded_t(ctypes.Structure):
+    _fields_ = [("shards", ctypes.POINTER(dmuon_shard_t)), ("nshards", ctypes.c_int32),
+                ("split", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _I64P = ctypes.POINTER(ctypes.c_int64)
@@ -80,6 +90,10 @@ EXPORTS = {
     "dmuon_orthogonalize_workspace_size": (ctypes.c_size_t, [_I64P, _I64P, ctypes.c_int32, _HP]),
     "dmuon_orthogonalize": (ctypes.c_int, [_PP, _PP, _I64P, _I64P, ctypes.c_int32, ctypes.c_int32,
                                            _HP, _P, ctypes.c_size_t, _P]),
+    "dmuon_orthogonalize_sharded_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(dmuon_sharded_t),
+                                                                      ctypes.c_int32, _HP]),
+    "dmuon_orthogonalize_sharded": (ctypes.c_int, [ctypes.POINTER(dmuon_sharded_t), ctypes.c_int32,
+                                                   ctypes.c_int32, _HP, _P, ctypes.c_size_t, _P]),
     "dmuon_apply_update_workspace_size": (ctypes.c_size_t, [ctypes.c_int32]),
     "dmuon_apply_update": (ctypes.c_int, [_MP, ctypes.c_int32, _PP, ctypes.c_int32, _HP, _P,
                                           ctypes.c_size_t, _P]),
@@ -302,6 +316,69 @@ def dmuon_orthogonalize(inputs: List[torch.Tensor], outputs: List[torch.Tensor],
     _check(_lib.dmuon_orthogonalize(_ptrs(inputs), _ptrs(outputs), rows, cols, n, dt, ctypes.byref(h),
                                     ws.data_ptr() if ws is not None else None, wsb,
                                     _stream(stream, inputs[0].device)), "dmuon_orthogonalize")
+
+
+def _sharded(shards: Sequence[Sequence[Tuple[int, int]]], splits: Sequence[int],
+             ins=None, outs=None):
+    """ctypes descriptors of sharded matrices (shapes, and device pointers
+    when tensors are given); returns (array, objects to keep alive)."""
+    n = len(shards)
+    arr = (dmuon_sharded_t * max(n, 1))()
+    keep = []
+    for i, mat in enumerate(shards):
+        sh = (dmuon_shard_t * max(len(mat), 1))()
+        for j, (r, c) in enumerate(mat):
+            sh[j].rows, sh[j].cols = int(r), int(c)
+            if ins is not None:
+                sh[j].in_ = ins[i][j].data_ptr()
+                sh[j].out = outs[i][j].data_ptr()
+        keep.append(sh)
+        arr[i].shards = ctypes.cast(sh, ctypes.POINTER(dmuon_shard_t))
+        arr[i].nshards = len(mat)
+        arr[i].split = int(splits[i])
+    return arr, keep
+
+
+def _splits(split, n: int) -> List[int]:
+    return [int(split)] * n if isinstance(split, int) else [int(v) for v in split]
+
+
+def dmuon_orthogonalize_sharded_workspace_size(shards: Sequence[Sequence[Sequence[int]]], split=1,
+                                               **hp) -> int:
+    """Workspace bytes of dmuon_orthogonalize_sharded for these shard shapes."""
+    arr, _k1 = _sharded(shards, _splits(split, len(shards)))
+    h, _k2 = _hparams(**hp)
+    return int(_lib.dmuon_orthogonalize_sharded_workspace_size(arr, len(shards), ctypes.byref(h)))
+
+
+def dmuon_orthogonalize_sharded(inputs: List[List[torch.Tensor]], outputs: List[List[torch.Tensor]],
+                                split=1, *, workspace: Optional[torch.Tensor] = None, stream=None,
+                                **hp) -> None:
+    """outputs[i][s] = shard s of NS(U_i), where U_i is the matrix whose
+    column blocks (split = 1) or row blocks (split = 0) are inputs[i]
+    (``split`` one value or one per matrix); the Gram matrices of the shards
+    are summed, the shards themselves are never joined."""
+    n = len(inputs)
+    if n == 0:
+        return
+    dt = _dtype(inputs[0][0])
+    for i in range(n):
+        if len(outputs[i]) != len(inputs[i]):
+            raise ValueError(f"outputs[{i}] must have one tensor per shard")
+        for j, (a, b) in enumerate(zip(inputs[i], outputs[i])):
+            _mat(a, f"inputs[{i}][{j}]")
+            _mat(b, f"outputs[{i}][{j}]")
+            if _dtype(a) != dt or _dtype(b) != dt or a.shape != b.shape:
+                raise ValueError(f"inputs[{i}][{j}] / outputs[{i}][{j}] must share one shape and dtype")
+    shapes = [[tuple(t.shape) for t in mat] for mat in inputs]
+    arr, _keep = _sharded(shapes, _splits(split, n), inputs, outputs)
+    h, _keep2 = _hparams(**hp)
+    nbytes = int(_lib.dmuon_orthogonalize_sharded_workspace_size(arr, n, ctypes.byref(h)))
+    dev = inputs[0][0].device
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    _check(_lib.dmuon_orthogonalize_sharded(arr, n, dt, ctypes.byref(h),
+                                            ws.data_ptr() if ws is not None else None, wsb,
+                                            _stream(stream, dev)), "dmuon_orthogonalize_sharded")
 
 
 def dmuon_apply_update(params: List[torch.Tensor], updates: List[torch.Tensor], *, lr: float = 0.02,

@@ -108,12 +108,29 @@ struct MatLayout {
   int64_t rows, cols, m, n, mp, np;
   int64_t pm, pn; // row pitches (elements) of the buffers whose rows hold mp / np values
   int64_t tile;   // GEMM tile edge of this matrix's products (mp, np are multiples)
-  bool tall;
+  bool tall;      // the wide (m x n) orientation is the transpose of the stored one
   Form form;
   // byte offsets into the workspace (SIZE_MAX when unused); *t buffers hold
-  // the transposes (n_pad x m_pad) of the m_pad x n_pad ones
-  size_t x0, x0t, x1, x1t, o, a, b, p, t, q0, q1;
+  // the transposes (n_pad x m_pad) of the m_pad x n_pad ones; r is a shard's
+  // partial Gram matrix (sharded matrices of more than one shard only)
+  size_t x0, x0t, x1, x1t, o, a, b, p, t, q0, q1, r;
   size_t out;  // where O is left
+};
+
+// One matrix of a call, or one shard of a sharded matrix.  The wide
+// orientation is rows x cols, or its transpose when `tall`.
+struct ShapeSpec {
+  int64_t rows, cols;
+  bool tall;
+};
+
+// Consecutive entries first .. first + count - 1 form one matrix: its shards
+// share the wide row count d, and the matrix's wide column count is the sum
+// of theirs (count 1: an ordinary matrix).
+struct Group {
+  int first, count;
+  int64_t d, D;
+  Form form;
 };
 
 // One GEMM as planned: pointers are workspace byte offsets.
@@ -122,13 +139,23 @@ struct Op {
   int tile;
   size_t A, B, C, Ct, Y;  // Ct, Y == SIZE_MAX: none
   int64_t lda, ldb, ldc, ldct, ldy;
+  int64_t kr;             // true (unpadded) contraction length
   int32_t K, tiles_m, tiles_n, sym, alpha_pow, beta_pow, diag_limit;
   float alpha, beta, gamma;
   bool scaled;
 };
 
+// One sum of partial Gram matrices, run after the GEMM launches of `stage`.
+struct SumPlan {
+  int stage;
+  size_t dst;
+  int64_t ld, edge;
+  std::vector<size_t> parts;
+};
+
 struct Launch {
   int tile;
+  int stage;
   int first;   // index into Plan::ops (sorted order)
   int count;
   int64_t tiles;
@@ -143,14 +170,18 @@ struct Plan {
   int ns_steps = 0;
   int tile = 0;
   std::vector<MatLayout> mats;
+  std::vector<Group> groups;
   std::vector<Op> ops;            // grouped by launch
   std::vector<Launch> launches;
   std::vector<TileRef> tile_map;  // all launches' block -> (task, tile) maps
+  std::vector<SumPlan> sums;      // ordered by stage
+  int64_t sum_parts = 0;
   std::vector<int64_t> blk_wide, blk_stored;
   int64_t blocks_wide = 0, blocks_stored = 0;
   // workspace layout
-  size_t off_ewmats = 0, off_tasks = 0, off_map = 0, off_partials = 0, off_sumsq = 0, off_scale = 0;
-  size_t table_bytes = 0;   // EwMat[] + GemmTask[] + TileRef[]
+  size_t off_ewmats = 0, off_tasks = 0, off_map = 0, off_sums = 0, off_sum_parts = 0;
+  size_t off_partials = 0, off_sumsq = 0, off_scale = 0;
+  size_t table_bytes = 0;   // EwMat[] + GemmTask[] + TileRef[] + GramSum[] + part pointers
   size_t ws_bytes = 0;
 };
 
@@ -164,9 +195,11 @@ int gemm_tile_override() {
   return (t == kTileBf16 || t == kTileBf16Big) ? t : 0;
 }
 
-std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n, int32_t prec,
-                                 int32_t backend, const Coeffs& cf, bool with_ns, int tile_override) {
+std::shared_ptr<Plan> build_plan(const std::vector<ShapeSpec>& shapes, const std::vector<Group>& groups_in,
+                                 int32_t prec, int32_t backend, const Coeffs& cf, bool with_ns,
+                                 int tile_override) {
   auto P = std::make_shared<Plan>();
+  const int n = static_cast<int>(shapes.size());
   P->n = n;
   P->prec = prec;
   P->ns_steps = with_ns ? static_cast<int>(cf.abc.size() / 3) : 0;
@@ -176,8 +209,8 @@ std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n
   // tiles in the first (X X^T) stage -- and 128 otherwise; matrices narrower
   // than 256 always use 128.
   int64_t big_tiles = 0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t t = (std::min(rows[i], cols[i]) + kTileBf16Big - 1) / kTileBf16Big;
+  for (const ShapeSpec& s : shapes) {
+    const int64_t t = ((s.tall ? s.cols : s.rows) + kTileBf16Big - 1) / kTileBf16Big;
     big_tiles += t * (t + 1) / 2;
   }
   bool use_big = prec == DMUON_NS_PREC_BF16 && big_tiles >= kBigTileMinCount;
@@ -186,127 +219,181 @@ std::shared_ptr<Plan> build_plan(const int64_t* rows, const int64_t* cols, int n
   P->blk_wide.resize(n);
   P->blk_stored.resize(n);
   P->mats.resize(n);
-  std::vector<std::vector<std::vector<Op>>> stages(n);
-  for (int i = 0; i < n; ++i) {
-    MatLayout& L = P->mats[i];
-    L.rows = rows[i];
-    L.cols = cols[i];
-    L.tall = rows[i] > cols[i];
-    L.m = std::min(rows[i], cols[i]);
-    L.n = std::max(rows[i], cols[i]);
-    L.tile = prec == DMUON_NS_PREC_BF16 ? ((use_big && L.m >= 256) ? kTileBf16Big : kTileBf16)
-                                        : kTileF32;
-    L.mp = with_ns ? round_up(L.m, L.tile) : L.m;
-    L.np = with_ns ? round_up(L.n, L.tile) : L.n;
-    // one extra 128-byte line per row: rows of a power-of-two-like pitch
-    // would otherwise start at the same offsets of the L2 channel
-    // interleave, and a k-slice of a panel would land on a few channels
-    L.pm = with_ns ? L.mp + kPitchPad : L.mp;
-    L.pn = with_ns ? L.np + kPitchPad : L.np;
-    L.form = choose_form(backend, L.m, L.n);
-    L.x0 = L.x0t = L.x1 = L.x1t = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = kNone;
-    P->blk_wide[i] = P->blocks_wide;
-    P->blocks_wide += ((L.mp + kEwTile - 1) / kEwTile) * ((L.np + kEwTile - 1) / kEwTile);
-    P->blk_stored[i] = P->blocks_stored;
-    P->blocks_stored += ((L.rows + kEwTile - 1) / kEwTile) * ((L.cols + kEwTile - 1) / kEwTile);
+  P->groups = groups_in;
+  for (Group& g : P->groups) {
+    g.d = shapes[g.first].tall ? shapes[g.first].cols : shapes[g.first].rows;
+    g.D = 0;
+    for (int i = g.first; i < g.first + g.count; ++i) g.D += shapes[i].tall ? shapes[i].rows : shapes[i].cols;
+    g.form = choose_form(backend, g.d, g.D);
+    for (int i = g.first; i < g.first + g.count; ++i) {
+      MatLayout& L = P->mats[i];
+      L.rows = shapes[i].rows;
+      L.cols = shapes[i].cols;
+      L.tall = shapes[i].tall;
+      L.m = g.d;
+      L.n = L.tall ? L.rows : L.cols;
+      L.tile = prec == DMUON_NS_PREC_BF16 ? ((use_big && g.d >= 256) ? kTileBf16Big : kTileBf16)
+                                          : kTileF32;
+      L.mp = with_ns ? round_up(L.m, L.tile) : L.m;
+      L.np = with_ns ? round_up(L.n, L.tile) : L.n;
+      // one extra 128-byte line per row: rows of a power-of-two-like pitch
+      // would otherwise start at the same offsets of the L2 channel
+      // interleave, and a k-slice of a panel would land on a few channels
+      L.pm = with_ns ? L.mp + kPitchPad : L.mp;
+      L.pn = with_ns ? L.np + kPitchPad : L.np;
+      L.form = g.form;
+      L.x0 = L.x0t = L.x1 = L.x1t = L.o = L.a = L.b = L.p = L.t = L.q0 = L.q1 = L.r = L.out = kNone;
+      P->blk_wide[i] = P->blocks_wide;
+      P->blocks_wide += ((L.mp + kEwTile - 1) / kEwTile) * ((L.np + kEwTile - 1) / kEwTile);
+      P->blk_stored[i] = P->blocks_stored;
+      P->blocks_stored += ((L.rows + kEwTile - 1) / kEwTile) * ((L.cols + kEwTile - 1) / kEwTile);
+    }
   }
   return P;  // buffers are laid out by layout_plan()
 }
 
-// Per-matrix stage lists of the NS iteration.  Every product is
-// C = alpha * A B^T (+ beta Y + gamma I) with K-contiguous operands; the
-// m x n operand of the left-multiplications comes from its transpose.
+Op base_op(int mat, int64_t tile) {
+  Op o{};
+  o.mat = mat; o.tile = static_cast<int>(tile);
+  o.Ct = kNone; o.Y = kNone; o.ldct = 0; o.ldy = 0;
+  o.alpha = 1.f; o.beta = 0.f; o.gamma = 0.f; o.diag_limit = 0;
+  o.alpha_pow = o.beta_pow = 0; o.scaled = false;
+  return o;
+}
+
+// Symmetric d x d result A B^T of two row-major operands with leading
+// dimension ldab and padded contraction length Kpad (true length kr).
+Op sym_op(int mat, const MatLayout& G, size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int64_t Kpad,
+          int64_t kr) {
+  Op o = base_op(mat, G.tile);
+  o.A = A; o.B = B; o.C = C; o.Y = Y;
+  o.lda = o.ldb = ldab; o.ldc = G.pm; o.ldy = G.pm;
+  o.K = static_cast<int32_t>(Kpad); o.kr = kr;
+  o.tiles_m = o.tiles_n = static_cast<int32_t>(G.mp / G.tile); o.sym = 1;
+  return o;
+}
+
+// d x n_i result M . X of one matrix or shard S, where M is d x d and X^T
+// (n_i x d) is stored.
+Op left_op(int mat, const MatLayout& S, size_t M, size_t Xt, size_t C, size_t Ct) {
+  Op o = base_op(mat, S.tile);
+  o.A = M; o.B = Xt; o.C = C; o.Ct = Ct;
+  o.lda = S.pm; o.ldb = S.pm; o.ldc = S.pn; o.ldct = S.pm;
+  o.K = static_cast<int32_t>(S.mp); o.kr = S.m;
+  o.tiles_m = static_cast<int32_t>(S.mp / S.tile);
+  o.tiles_n = static_cast<int32_t>(S.np / S.tile);
+  o.sym = 0;
+  return o;
+}
+
+// Stage lists of the NS iteration, per group (kept on the group's first
+// entry).  Every product is C = alpha * A B^T (+ beta Y + gamma I) with
+// K-contiguous operands; the m x n operand of the left-multiplications comes
+// from its transpose.  A group of several shards forms its Gram matrices as
+// one partial product per shard followed by their sum (a SumPlan after that
+// stage): once (Gram form) or every iteration (direct form); the d x d
+// products run once per group and the left products once per shard.
 void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>>>& stages) {
   const int K = P.ns_steps;
   stages.assign(P.n, {});
-  for (int i = 0; i < P.n; ++i) {
-    MatLayout& L = P.mats[i];
-    const int64_t T = L.tile;
-    auto& st = stages[i];
-    if (K == 0) { L.out = L.x0; continue; }
-    const int32_t tm_mm = static_cast<int32_t>(L.mp / T);
-    const int32_t tn_mn = static_cast<int32_t>(L.np / T);
-    auto base_op = [&]() {
-      Op o{};
-      o.mat = i; o.tile = static_cast<int>(T);
-      o.Ct = kNone; o.Y = kNone; o.ldct = 0; o.ldy = 0;
-      o.alpha = 1.f; o.beta = 0.f; o.gamma = 0.f; o.diag_limit = 0;
-      o.alpha_pow = o.beta_pow = 0; o.scaled = false;
-      return o;
+  P.sums.clear();
+  for (const Group& g : P.groups) {
+    const int f = g.first, e = g.first + g.count;
+    MatLayout& G = P.mats[f];
+    auto& st = stages[f];
+    if (K == 0) {
+      for (int i = f; i < e; ++i) P.mats[i].out = P.mats[i].x0;
+      continue;
+    }
+    // the Gram products of every shard of stage `stage`, into A directly for
+    // a single shard, else into the shards' partial buffers and then summed
+    auto gram_products = [&](int stage, const size_t* xin, bool first) {
+      std::vector<Op> ops;
+      for (int i = f; i < e; ++i) {
+        const MatLayout& S = P.mats[i];
+        Op o = sym_op(i, G, xin[i - f], xin[i - f], g.count > 1 ? S.r : G.a, kNone, S.pn, S.np, S.n);
+        if (first) { o.alpha_pow = 2; o.scaled = true; }
+        ops.push_back(o);
+      }
+      if (g.count > 1) {
+        SumPlan sp;
+        sp.stage = stage; sp.dst = G.a; sp.ld = G.pm; sp.edge = G.mp;
+        for (int i = f; i < e; ++i) sp.parts.push_back(P.mats[i].r);
+        P.sums.push_back(sp);
+      }
+      return ops;
     };
-    // symmetric m x m result of two row-major operands with leading dim ldab
-    auto sym_op = [&](size_t A, size_t B, size_t C, size_t Y, int64_t ldab, int64_t Kdim) {
-      Op o = base_op();
-      o.A = A; o.B = B; o.C = C; o.Y = Y;
-      o.lda = o.ldb = ldab; o.ldc = L.pm; o.ldy = L.pm;
-      o.K = static_cast<int32_t>(Kdim); o.tiles_m = o.tiles_n = tm_mm; o.sym = 1;
-      return o;
-    };
-    // m x n result M . X where M is m x m and X^T (n x m) is stored
-    auto left_op = [&](size_t M, size_t Xt, size_t C, size_t Ct) {
-      Op o = base_op();
-      o.A = M; o.B = Xt; o.C = C; o.Ct = Ct;
-      o.lda = L.pm; o.ldb = L.pm; o.ldc = L.pn; o.ldct = L.pm;
-      o.K = static_cast<int32_t>(L.mp); o.tiles_m = tm_mm; o.tiles_n = tn_mn; o.sym = 0;
-      return o;
-    };
-    if (L.form == FORM_DIRECT) {
-      const size_t xb[2] = {L.x0, L.x1}, xtb[2] = {L.x0t, L.x1t};
+    std::vector<size_t> x0(g.count), x0t(g.count), x1(g.count), x1t(g.count);
+    for (int i = f; i < e; ++i) {
+      x0[i - f] = P.mats[i].x0; x0t[i - f] = P.mats[i].x0t;
+      x1[i - f] = P.mats[i].x1; x1t[i - f] = P.mats[i].x1t;
+    }
+    if (g.form == FORM_DIRECT) {
+      const std::vector<size_t>* xb[2] = {&x0, &x1};
+      const std::vector<size_t>* xtb[2] = {&x0t, &x1t};
       for (int k = 0; k < K; ++k) {
         const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
-        const size_t xin = xb[k % 2], xin_t = xtb[k % 2];
-        const size_t xout = xb[(k + 1) % 2], xout_t = xtb[(k + 1) % 2];
+        const std::vector<size_t>& xin = *xb[k % 2];
+        const std::vector<size_t>& xin_t = *xtb[k % 2];
+        const std::vector<size_t>& xout = *xb[(k + 1) % 2];
+        const std::vector<size_t>& xout_t = *xtb[(k + 1) % 2];
         // A = s^2 X X^T (s folded in on the first step only)
-        Op g = sym_op(xin, xin, L.a, kNone, L.pn, L.np);
-        if (k == 0) { g.alpha_pow = 2; g.scaled = true; }
-        st.push_back({g});
+        st.push_back(gram_products(static_cast<int>(st.size()), xin.data(), k == 0));
         // B = b A + c A A
-        Op h = sym_op(L.a, L.a, L.b, L.a, L.pm, L.mp);
+        Op h = sym_op(f, G, G.a, G.a, G.b, G.a, G.pm, G.mp, G.m);
         h.alpha = static_cast<float>(c);
         h.beta = static_cast<float>(b);
         st.push_back({h});
         // X' = a X + B X, and X'^T for the next step's left product
-        Op u = left_op(L.b, xin_t, xout, k + 1 < K ? xout_t : kNone);
-        u.Y = xin; u.ldy = L.pn;
-        u.beta = static_cast<float>(a);
-        u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0;
-        u.scaled = (k == 0);
-        st.push_back({u});
+        std::vector<Op> upd;
+        for (int i = f; i < e; ++i) {
+          const MatLayout& S = P.mats[i];
+          Op u = left_op(i, S, G.b, xin_t[i - f], xout[i - f], k + 1 < K ? xout_t[i - f] : kNone);
+          u.Y = xin[i - f]; u.ldy = S.pn;
+          u.beta = static_cast<float>(a);
+          u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0;
+          u.scaled = (k == 0);
+          upd.push_back(u);
+        }
+        st.push_back(upd);
       }
-      L.out = xb[K % 2];
+      for (int i = f; i < e; ++i) P.mats[i].out = (*xb[K % 2])[i - f];
     } else {
       // R = s^2 X0 X0^T, kept in A
-      Op r = sym_op(L.x0, L.x0, L.a, kNone, L.pn, L.np);
-      r.alpha_pow = 2; r.scaled = true;
-      st.push_back({r});
-      const size_t qbuf[2] = {L.q0, L.q1};
+      st.push_back(gram_products(0, x0.data(), true));
+      const size_t qbuf[2] = {G.q0, G.q1};
       for (int k = 0; k < K; ++k) {
         const double a = cf.abc[3 * k], b = cf.abc[3 * k + 1], c = cf.abc[3 * k + 2];
-        const size_t pk = (k == 0) ? L.q0 : L.p;   // P_0 is Q itself
-        Op pp = sym_op(L.a, L.a, pk, L.a, L.pm, L.mp);
+        const size_t pk = (k == 0) ? G.q0 : G.p;   // P_0 is Q itself
+        Op pp = sym_op(f, G, G.a, G.a, pk, G.a, G.pm, G.mp, G.m);
         pp.alpha = static_cast<float>(c);
         pp.beta = static_cast<float>(b);
         pp.gamma = static_cast<float>(a);
-        pp.diag_limit = static_cast<int32_t>(L.m);
+        pp.diag_limit = static_cast<int32_t>(G.m);
         st.push_back({pp});
         std::vector<Op> next;
-        if (k >= 1) next.push_back(sym_op(pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, L.pm, L.mp));  // Q <- P Q
-        if (k + 1 < K) next.push_back(sym_op(pk, L.a, L.t, kNone, L.pm, L.mp));                     // T = P A
+        if (k >= 1) next.push_back(sym_op(f, G, pk, qbuf[(k - 1) % 2], qbuf[k % 2], kNone, G.pm, G.mp, G.m));  // Q <- P Q
+        if (k + 1 < K) next.push_back(sym_op(f, G, pk, G.a, G.t, kNone, G.pm, G.mp, G.m));                     // T = P A
         if (!next.empty()) st.push_back(next);
-        if (k + 1 < K) st.push_back({sym_op(L.t, pk, L.a, kNone, L.pm, L.mp)});                     // A = T P
+        if (k + 1 < K) st.push_back({sym_op(f, G, G.t, pk, G.a, kNone, G.pm, G.mp, G.m)});                     // A = T P
       }
-      Op f = left_op(qbuf[(K - 1) % 2], L.x0t, L.o, kNone);                                            // O = s Q X0
-      f.alpha_pow = 1; f.scaled = true;
-      st.push_back({f});
-      L.out = L.o;
+      std::vector<Op> fin;
+      for (int i = f; i < e; ++i) {
+        MatLayout& S = P.mats[i];
+        Op o = left_op(i, S, qbuf[(K - 1) % 2], S.x0t, S.o, kNone);                                            // O = s Q X0
+        o.alpha_pow = 1; o.scaled = true;
+        fin.push_back(o);
+        S.out = S.o;
+      }
+      st.push_back(fin);
     }
   }
+  std::stable_sort(P.sums.begin(), P.sums.end(), [](const SumPlan& x, const SumPlan& y) { return x.stage < y.stage; });
 }
 
 int64_t op_tiles(const Op& o) {
   return o.sym ? int64_t(o.tiles_m) * (o.tiles_m + 1) / 2 : int64_t(o.tiles_m) * o.tiles_n;
 }
-
 // Output tiles of one product in the order one XCD walks them: groups of
 // kTileGroupRows x kTileGroupCols tiles, group-row by group-row, so the tiles
 // an XCD runs at once share their A and B panels; symmetric products keep
@@ -378,27 +465,37 @@ void build_tile_maps(Plan& P) {
 // Lay out workspace buffers and group ops into launches.
 void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   const size_t es = P.prec == DMUON_NS_PREC_BF16 ? 2 : 4;
-  // buffers
+  // buffers: per group, its shards' own buffers, then the group's d x d ones
   size_t cur = 0;  // relative to the start of the matrix region
-  for (auto& L : P.mats) {
-    const size_t mn = align_up(size_t(L.mp) * L.pn * es);    // m x n, pitch pn
-    const size_t mnt = align_up(size_t(L.np) * L.pm * es);   // n x m, pitch pm
-    const size_t mm = align_up(size_t(L.mp) * L.pm * es);    // m x m, pitch pm
-    L.x0 = cur; cur += mn;
-    if (!with_ns || P.ns_steps == 0) continue;
-    L.x0t = cur; cur += mnt;
-    if (L.form == FORM_DIRECT) {
-      L.x1 = cur; cur += mn;
-      if (P.ns_steps > 1) { L.x1t = cur; cur += mnt; }
-      L.a = cur; cur += mm;
-      L.b = cur; cur += mm;
+  const bool ns = with_ns && P.ns_steps > 0;
+  for (const Group& g : P.groups) {
+    for (int i = g.first; i < g.first + g.count; ++i) {
+      MatLayout& L = P.mats[i];
+      const size_t mn = align_up(size_t(L.mp) * L.pn * es);    // m x n, pitch pn
+      const size_t mnt = align_up(size_t(L.np) * L.pm * es);   // n x m, pitch pm
+      L.x0 = cur; cur += mn;
+      if (!ns) continue;
+      L.x0t = cur; cur += mnt;
+      if (L.form == FORM_DIRECT) {
+        L.x1 = cur; cur += mn;
+        if (P.ns_steps > 1) { L.x1t = cur; cur += mnt; }
+      } else {
+        L.o = cur; cur += mn;
+      }
+      if (g.count > 1) { L.r = cur; cur += align_up(size_t(L.mp) * L.pm * es); }
+    }
+    if (!ns) continue;
+    MatLayout& G = P.mats[g.first];
+    const size_t mm = align_up(size_t(G.mp) * G.pm * es);    // d x d, pitch pm
+    if (G.form == FORM_DIRECT) {
+      G.a = cur; cur += mm;
+      G.b = cur; cur += mm;
     } else {
-      L.o = cur; cur += mn;
-      L.a = cur; cur += mm;
-      L.p = cur; cur += mm;
-      L.t = cur; cur += mm;
-      L.q0 = cur; cur += mm;
-      L.q1 = cur; cur += mm;
+      G.a = cur; cur += mm;
+      G.p = cur; cur += mm;
+      G.t = cur; cur += mm;
+      G.q0 = cur; cur += mm;
+      G.q1 = cur; cur += mm;
     }
   }
   const size_t mat_region = cur;
@@ -421,7 +518,8 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
             if (o.tile == tile) group.push_back(o);
       if (group.empty()) continue;
       std::stable_sort(group.begin(), group.end(), [](const Op& x, const Op& y) { return x.K > y.K; });
-      Launch l{tile, static_cast<int>(P.ops.size()), static_cast<int>(group.size()), 0, 0, 0, 0};
+      Launch l{tile, static_cast<int>(s), static_cast<int>(P.ops.size()), static_cast<int>(group.size()),
+               0, 0, 0, 0};
       const int64_t es = P.prec == DMUON_NS_PREC_BF16 ? 2 : 4;
       for (auto& o : group) {
         l.tiles += op_tiles(o);
@@ -429,9 +527,8 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
         const int64_t m = L.m, n = L.n;
         const bool has_y = o.Y != kNone;
         if (o.sym) {
-          const int64_t kr = (o.K == L.np) ? n : m;   // X X^T reads m x n, others m x m
-          l.alg_flops += m * (m + 1) * kr;
-          l.alg_bytes += es * (m * kr * (o.A == o.B ? 1 : 2) + (has_y ? m * m : 0) + m * m);
+          l.alg_flops += m * (m + 1) * o.kr;
+          l.alg_bytes += es * (m * o.kr * (o.A == o.B ? 1 : 2) + (has_y ? m * m : 0) + m * m);
         } else {
           l.alg_flops += 2 * m * n * m;
           l.alg_bytes += es * (m * m + m * n + (has_y ? m * n : 0) + m * n * (o.Ct != kNone ? 2 : 1));
@@ -444,7 +541,10 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
 
   build_tile_maps(P);
 
-  // workspace: [EwMat table][GemmTask table][tile maps][partials][sumsq][scale][matrices]
+  // workspace: [EwMat table][GemmTask table][tile maps][Gram sums][their
+  // part pointers][partials][sumsq][scale][matrices]
+  P.sum_parts = 0;
+  for (const SumPlan& sp : P.sums) P.sum_parts += static_cast<int64_t>(sp.parts.size());
   size_t off = 0;
   P.off_ewmats = off;
   off += align_up(sizeof(EwMat) * std::max(P.n, 1));
@@ -452,6 +552,10 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   off += align_up(sizeof(GemmTask) * std::max<size_t>(P.ops.size(), 1));
   P.off_map = off;
   off += align_up(sizeof(TileRef) * std::max<size_t>(P.tile_map.size(), 1));
+  P.off_sums = off;
+  if (!P.sums.empty()) off += align_up(sizeof(GramSum) * P.sums.size());
+  P.off_sum_parts = off;
+  if (P.sum_parts > 0) off += align_up(sizeof(void*) * size_t(P.sum_parts));
   P.table_bytes = off;
   P.off_partials = off;
   off += align_up(sizeof(float) * std::max<int64_t>(P.blocks_wide, 1));
@@ -460,12 +564,16 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
   P.off_scale = off;
   off += align_up(sizeof(float) * std::max(P.n, 1));
   for (auto& L : P.mats) {
-    for (size_t* f : {&L.x0, &L.x0t, &L.x1, &L.x1t, &L.o, &L.a, &L.b, &L.p, &L.t, &L.q0, &L.q1, &L.out})
+    for (size_t* f : {&L.x0, &L.x0t, &L.x1, &L.x1t, &L.o, &L.a, &L.b, &L.p, &L.t, &L.q0, &L.q1, &L.r, &L.out})
       if (*f != kNone) *f += off;
   }
   for (auto& o : P.ops)
     for (size_t* f : {&o.A, &o.B, &o.C, &o.Ct, &o.Y})
       if (*f != kNone) *f += off;
+  for (auto& sp : P.sums) {
+    sp.dst += off;
+    for (size_t& q : sp.parts) q += off;
+  }
   P.ws_bytes = off + mat_region;
 }
 
@@ -476,31 +584,50 @@ void layout_plan(Plan& P, const Coeffs& cf, bool with_ns) {
 std::mutex g_plan_mu;
 std::unordered_map<std::string, std::shared_ptr<Plan>> g_plans;
 
-std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
+std::shared_ptr<Plan> get_plan(const std::vector<ShapeSpec>& shapes, const std::vector<Group>& groups,
                                int32_t prec, int32_t backend, const Coeffs& cf, bool with_ns) {
   std::string key;
-  key.reserve(32 + rows.size() * 16 + cf.abc.size() * 8);
+  key.reserve(32 + shapes.size() * 24 + groups.size() * 8 + cf.abc.size() * 8);
   auto put = [&](const void* p, size_t n) { key.append(static_cast<const char*>(p), n); };
   const int tile_override = gemm_tile_override();
   const int32_t hdr[4] = {prec, with_ns ? backend : -1, with_ns ? 1 : 0, tile_override};
   put(hdr, sizeof(hdr));
-  const int64_t n = static_cast<int64_t>(rows.size());
+  const int64_t n = static_cast<int64_t>(shapes.size()), ng = static_cast<int64_t>(groups.size());
   put(&n, sizeof(n));
-  put(rows.data(), rows.size() * sizeof(int64_t));
-  put(cols.data(), cols.size() * sizeof(int64_t));
+  put(&ng, sizeof(ng));
+  for (const ShapeSpec& s : shapes) {
+    const int64_t v[3] = {s.rows, s.cols, s.tall ? 1 : 0};
+    put(v, sizeof(v));
+  }
+  for (const Group& g : groups) {
+    const int32_t v[2] = {g.first, g.count};
+    put(v, sizeof(v));
+  }
   if (with_ns) put(cf.abc.data(), cf.abc.size() * sizeof(double));
   {
     std::lock_guard<std::mutex> lk(g_plan_mu);
     auto it = g_plans.find(key);
     if (it != g_plans.end()) return it->second;
   }
-  auto P = build_plan(rows.data(), cols.data(), static_cast<int>(rows.size()), prec, backend, cf, with_ns,
-                      tile_override);
+  auto P = build_plan(shapes, groups, prec, backend, cf, with_ns, tile_override);
   layout_plan(*P, cf, with_ns);
   std::lock_guard<std::mutex> lk(g_plan_mu);
   if (g_plans.size() > 256) g_plans.clear();
   g_plans.emplace(key, P);
   return P;
+}
+
+// The plan of independent whole matrices: each in its wide orientation
+// (transposed when tall), one group each.
+std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
+                               int32_t prec, int32_t backend, const Coeffs& cf, bool with_ns) {
+  std::vector<ShapeSpec> shapes(rows.size());
+  std::vector<Group> groups(rows.size());
+  for (size_t i = 0; i < rows.size(); ++i) {
+    shapes[i] = {rows[i], cols[i], rows[i] > cols[i]};
+    groups[i] = {static_cast<int>(i), 1, 0, 0, FORM_DIRECT};
+  }
+  return get_plan(shapes, groups, prec, backend, cf, with_ns);
 }
 
 // ---------------------------------------------------------------------------
@@ -583,9 +710,9 @@ int check_device() {
 // ---------------------------------------------------------------------------
 
 enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_BF16, PK_GEMM_F32, PK_UPDATE,
-                PK_CLIP_NORM, PK_CLIP_FINALIZE, PK_CLIP_SCALE, PK_COUNT };
+                PK_CLIP_NORM, PK_CLIP_FINALIZE, PK_CLIP_SCALE, PK_GRAM_SUM, PK_COUNT };
 const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_bf16", "gemm_f32", "update",
-                                          "clip_norm", "clip_finalize", "clip_scale"};
+                                          "clip_norm", "clip_finalize", "clip_scale", "gram_sum"};
 
 struct ProfRec {
   int kind;
@@ -662,18 +789,62 @@ void fill_tasks(const Plan& P, char* ws_base, GemmTask* out) {
   if (!P.tile_map.empty())
     std::memcpy(reinterpret_cast<char*>(out) + (P.off_map - P.off_tasks), P.tile_map.data(),
                 sizeof(TileRef) * P.tile_map.size());
+  // Gram sums: entries of one stage are contiguous; blk_first counts from
+  // the first entry of that stage (one launch per stage)
+  GramSum* sums = reinterpret_cast<GramSum*>(reinterpret_cast<char*>(out) + (P.off_sums - P.off_tasks));
+  void** parts = reinterpret_cast<void**>(reinterpret_cast<char*>(out) + (P.off_sum_parts - P.off_tasks));
+  int32_t part = 0;
+  int64_t blk = 0;
+  for (size_t j = 0; j < P.sums.size(); ++j) {
+    const SumPlan& sp = P.sums[j];
+    if (j == 0 || P.sums[j - 1].stage != sp.stage) blk = 0;
+    GramSum& g = sums[j];
+    g.dst = ws_base + sp.dst;
+    g.ld = sp.ld;
+    g.blk_first = blk;
+    g.edge = static_cast<int32_t>(sp.edge);
+    g.first_part = part;
+    g.count = static_cast<int32_t>(sp.parts.size());
+    for (size_t q : sp.parts) parts[part++] = ws_base + q;
+    blk += (sp.edge / kEwTile) * (sp.edge / kEwTile);
+  }
 }
 
+// The GEMM launches in stage order; after the last launch of a stage, the
+// Gram sums planned for that stage (sharded matrices only).
 int run_gemms(const Plan& P, char* ws, hipStream_t stream) {
   const GemmTask* tasks = reinterpret_cast<const GemmTask*>(ws + P.off_tasks);
   const TileRef* map = reinterpret_cast<const TileRef*>(ws + P.off_map);
-  for (const Launch& l : P.launches) {
-    const bool bf = P.prec == DMUON_NS_PREC_BF16;
+  const GramSum* sums = reinterpret_cast<const GramSum*>(ws + P.off_sums);
+  const void* const* parts = reinterpret_cast<const void* const*>(ws + P.off_sum_parts);
+  const bool bf = P.prec == DMUON_NS_PREC_BF16;
+  const int64_t es = bf ? 2 : 4;
+  size_t next_sum = 0;
+  for (size_t li = 0; li < P.launches.size(); ++li) {
+    const Launch& l = P.launches[li];
     hipError_t e = prof_launch(bf ? PK_GEMM_BF16 : PK_GEMM_F32, l.alg_flops, l.alg_bytes, stream, [&] {
       return bf ? launch_gemm_bf16(tasks + l.first, map + l.map_first, l.tiles, l.tile, stream)
                 : launch_gemm_f32(tasks + l.first, map + l.map_first, l.tiles, l.tile, stream);
     });
     if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("GEMM launch: ") + hipGetErrorString(e));
+    const bool stage_end = li + 1 == P.launches.size() || P.launches[li + 1].stage != l.stage;
+    if (!stage_end) continue;
+    size_t end = next_sum;
+    int64_t blocks = 0, bytes = 0;
+    while (end < P.sums.size() && P.sums[end].stage == l.stage) {
+      const SumPlan& sp = P.sums[end];
+      const int64_t tiles = (sp.edge / kEwTile) * (sp.edge / kEwTile);
+      blocks += tiles;
+      bytes += es * sp.edge * sp.edge * int64_t(sp.parts.size() + 1);
+      ++end;
+    }
+    if (end == next_sum) continue;
+    e = prof_launch(PK_GRAM_SUM, 0, bytes, stream, [&] {
+      return launch_gram_sum(sums + next_sum, static_cast<int>(end - next_sum), blocks, parts,
+                             bf ? DT_BF16 : DT_F32, stream);
+    });
+    if (e != hipSuccess) return fail(DMUON_ERR_HIP, std::string("Gram sum launch: ") + hipGetErrorString(e));
+    next_sum = end;
   }
   return DMUON_OK;
 }
@@ -1069,6 +1240,158 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
   st = run_gemms(P, ws, stream);
   if (st) return st;
   DMUON_HIP_TRY(launch_update(em_dev, P.n, P.blocks_stored, 1, scale, stream));
+  return DMUON_OK;
+}
+
+// ---- dmuon_orthogonalize_sharded ----------------------------------------------
+
+static int sharded_prepare(const dmuon_sharded_t* mats, int32_t n, const dmuon_hparams_t* hp, Coeffs* cf,
+                           std::shared_ptr<Plan>* plan) {
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !mats) return fail(DMUON_ERR_INVALID_ARG, "mats is NULL");
+  int st = check_hparams(hp, false, cf);
+  if (st) return st;
+  std::vector<ShapeSpec> shapes;
+  std::vector<Group> groups;
+  for (int i = 0; i < n; ++i) {
+    const dmuon_sharded_t& M = mats[i];
+    const std::string name = mat_name("mats", i);
+    if (M.nshards < 1) return fail(DMUON_ERR_INVALID_ARG, name + ".nshards must be >= 1");
+    if (M.split != 0 && M.split != 1) return fail(DMUON_ERR_INVALID_ARG, name + ".split must be 0 or 1");
+    if (!M.shards) return fail(DMUON_ERR_INVALID_ARG, name + ".shards is NULL");
+    if (shapes.size() + size_t(M.nshards) > size_t(1) << 30)
+      return fail(DMUON_ERR_INVALID_ARG, "too many shards");
+    groups.push_back({static_cast<int>(shapes.size()), M.nshards, 0, 0, FORM_DIRECT});
+    int64_t d = -1;
+    for (int s = 0; s < M.nshards; ++s) {
+      const dmuon_shard_t& S = M.shards[s];
+      if (S.rows <= 0 || S.cols <= 0 || S.rows > kMaxDim || S.cols > kMaxDim)
+        return fail(DMUON_ERR_INVALID_ARG, name + ".shards[" + std::to_string(s) + "]: bad shape");
+      const int64_t dd = M.split == 1 ? S.rows : S.cols;
+      if (d >= 0 && dd != d)
+        return fail(DMUON_ERR_INVALID_ARG, name + ".shards[" + std::to_string(s) +
+                                               "]: the unsplit dimension differs from shard 0's");
+      d = dd;
+      shapes.push_back({S.rows, S.cols, M.split == 0});
+    }
+  }
+  if (n == 0) return DMUON_OK;
+  *plan = get_plan(shapes, groups, hp->ns_precision, hp->ns_backend, *cf, true);
+  return DMUON_OK;
+}
+
+size_t dmuon_orthogonalize_sharded_workspace_size(const dmuon_sharded_t* mats, int32_t n,
+                                                  const dmuon_hparams_t* hp) {
+  Coeffs cf;
+  std::shared_ptr<Plan> plan;
+  if (sharded_prepare(mats, n, hp, &cf, &plan) != DMUON_OK || n == 0) return 0;
+  return plan->ws_bytes;
+}
+
+int dmuon_orthogonalize_sharded(const dmuon_sharded_t* mats, int32_t n, int32_t io_dtype,
+                                const dmuon_hparams_t* hp, void* workspace, size_t workspace_bytes,
+                                void* stream_) {
+  g_last_error.clear();
+  Coeffs cf;
+  std::shared_ptr<Plan> plan;
+  int st = sharded_prepare(mats, n, hp, &cf, &plan);
+  if (st) return st;
+  if (n == 0) return DMUON_OK;
+  if (!dtype_ok(io_dtype)) return fail(DMUON_ERR_UNSUPPORTED, "io_dtype must be F32 or BF16");
+  const Plan& P = *plan;
+  if (!workspace || workspace_bytes < P.ws_bytes) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "workspace needs %zu bytes, got %zu", P.ws_bytes, workspace_bytes);
+    return fail(DMUON_ERR_WORKSPACE, buf);
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  // the shards in plan order, with the index of their matrix
+  std::vector<const dmuon_shard_t*> sh;
+  std::vector<int> owner;
+  for (int i = 0; i < n; ++i)
+    for (int s = 0; s < mats[i].nshards; ++s) {
+      sh.push_back(&mats[i].shards[s]);
+      owner.push_back(i);
+    }
+  std::vector<Range> outs, ins;
+  const uintptr_t wlo = reinterpret_cast<uintptr_t>(workspace);
+  for (size_t j = 0; j < sh.size(); ++j) {
+    const std::string name = mat_name("mats", owner[j]) + ".shards[" +
+                             std::to_string(j - size_t(P.groups[owner[j]].first)) + "]";
+    if (!sh[j]->in || !sh[j]->out) return fail(DMUON_ERR_INVALID_ARG, name + ": in or out is NULL");
+    const size_t bytes = size_t(sh[j]->rows) * sh[j]->cols * dtype_size(io_dtype);
+    const uintptr_t o = reinterpret_cast<uintptr_t>(sh[j]->out), i = reinterpret_cast<uintptr_t>(sh[j]->in);
+    outs.push_back({o, o + bytes, name + ".out"});
+    ins.push_back({i, i + bytes, name + ".in"});
+  }
+  {
+    std::vector<Range> r = outs;
+    r.push_back({wlo, wlo + P.ws_bytes, "workspace"});
+    st = check_overlaps(r);
+    if (st) return st;
+    for (size_t i = 0; i < ins.size(); ++i) {
+      if (ins[i].lo < wlo + P.ws_bytes && wlo < ins[i].hi) return fail(DMUON_ERR_ALIASING, ins[i].what + " overlaps workspace");
+      for (size_t j = 0; j < outs.size(); ++j) {
+        if (i == j) {
+          if (ins[i].lo != outs[i].lo && ins[i].lo < outs[i].hi && outs[i].lo < ins[i].hi)
+            return fail(DMUON_ERR_ALIASING, ins[i].what + " partially overlaps " + outs[i].what);
+        } else if (ins[i].lo < outs[j].hi && outs[j].lo < ins[i].hi) {
+          return fail(DMUON_ERR_ALIASING, ins[i].what + " overlaps " + outs[j].what);
+        }
+      }
+    }
+  }
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
+  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+    EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
+    for (int j = 0; j < P.n; ++j) {
+      const MatLayout& L = P.mats[j];
+      const dmuon_shard_t& S = *sh[j];
+      const Group& g = P.groups[owner[j]];
+      EwMat& e = em[j];
+      e.rows = S.rows; e.cols = S.cols;
+      e.src = S.in; e.mom = nullptr; e.param = S.out;
+      e.u_dst = ws + L.x0; e.o_src = ws + L.out;
+      e.u_dst_t = L.x0t != kNone ? ws + L.x0t : nullptr; e.ld_wide_t = L.pm;
+      e.ld_wide = L.pn; e.wide_rows = static_cast<int32_t>(L.mp); e.wide_cols = static_cast<int32_t>(L.np);
+      e.tall = L.tall; e.src_dtype = io_dtype; e.wide_dtype = wide_dt; e.param_dtype = io_dtype;
+      e.scale_idx = P.ns_steps == 0 ? j : -1;
+      e.aligned = (S.cols % 4 == 0) && aligned16(S.in) && aligned16(S.out);
+      e.user_index = owner[j];
+      e.grp_first = g.first; e.grp_count = g.count;
+      e.blk_wide = P.blk_wide[j]; e.blk_stored = P.blk_stored[j];
+      e.lr_eff = 0.f; e.decay = 1.f;
+    }
+    fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks));
+  });
+  if (st) return st;
+  const EwMat* em_dev = reinterpret_cast<const EwMat*>(ws + P.off_ewmats);
+  float* partials = reinterpret_cast<float*>(ws + P.off_partials);
+  float* scale = reinterpret_cast<float*>(ws + P.off_scale);
+  double* sumsq = reinterpret_cast<double*>(ws + P.off_sumsq);
+  int64_t load_bytes = 0, store_bytes = 0;
+  for (int j = 0; j < P.n; ++j) {
+    const int64_t ne = sh[j]->rows * sh[j]->cols;
+    const int64_t outs_n = P.mats[j].x0t != kNone ? 2 : 1;
+    load_bytes += ne * (int64_t(dtype_size(io_dtype)) + outs_n * int64_t(dtype_size(wide_dt)));
+    store_bytes += ne * (int64_t(dtype_size(io_dtype)) + int64_t(dtype_size(wide_dt)));
+  }
+  DMUON_HIP_TRY(prof_launch(PK_MOMENTUM, 0, load_bytes, stream, [&] {
+    return launch_momentum(em_dev, P.n, P.blocks_wide, 1, 0.f, 0, partials, stream);
+  }));
+  DMUON_HIP_TRY(prof_launch(PK_FINALIZE, 0, P.blocks_wide * 4, stream, [&] {
+    return launch_finalize(em_dev, P.n, P.blocks_wide, partials, sumsq, scale, hp->eps, stream);
+  }));
+  st = run_gemms(P, ws, stream);
+  if (st) return st;
+  DMUON_HIP_TRY(prof_launch(PK_UPDATE, 0, store_bytes, stream, [&] {
+    return launch_update(em_dev, P.n, P.blocks_stored, 1, scale, stream);
+  }));
   return DMUON_OK;
 }
 

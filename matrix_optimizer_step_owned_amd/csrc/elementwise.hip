@@ -213,8 +213,13 @@ finalize_kernel(const EwMat* __restrict__ mats, int nmats, int64_t nblocks,
                 float* __restrict__ scale, double eps) {
   __shared__ double red[256];
   const int mi = blockIdx.x;
-  const int64_t b0 = mats[mi].blk_wide;
-  const int64_t b1 = mi + 1 < nmats ? mats[mi + 1].blk_wide : nblocks;
+  // a shard of a sharded matrix sums the blocks of all its group's shards
+  // (the same blocks in the same order for every member, so every shard
+  // gets the identical scale)
+  const int g0 = mats[mi].grp_count > 0 ? mats[mi].grp_first : mi;
+  const int g1 = mats[mi].grp_count > 0 ? mats[mi].grp_first + mats[mi].grp_count : mi + 1;
+  const int64_t b0 = mats[g0].blk_wide;
+  const int64_t b1 = g1 < nmats ? mats[g1].blk_wide : nblocks;
   double acc = 0.0;
   for (int64_t b = b0 + threadIdx.x; b < b1; b += 256) acc += static_cast<double>(partials[b]);
   red[threadIdx.x] = acc;
@@ -316,7 +321,53 @@ update_kernel(const EwMat* __restrict__ mats, int nmats, int mode, const float* 
   }
 }
 
+// Sum of partial Gram matrices (see GramSum).  Thread t covers tile rows
+// (t >> 4) + 16p and the four columns 4*(t & 15) .. +3, as the other
+// elementwise kernels; the parts are added in their order in fp32.
+__global__ void __launch_bounds__(kEwThreads)
+gram_sum_kernel(const GramSum* __restrict__ sums, int nsums, const void* const* __restrict__ parts,
+                int32_t dtype) {
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = nsums - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (sums[mid].blk_first <= b) lo = mid; else hi = mid - 1;
+  }
+  const GramSum S = sums[lo];
+  const int64_t local = b - S.blk_first;
+  const int tiles = S.edge / kEwTile;
+  const int64_t i0 = (local / tiles) * kEwTile, j0 = (local % tiles) * kEwTile;
+  const int t = threadIdx.x;
+  const int lc = (t & 15) * 4;
+  const int lr0 = t >> 4;
+  float acc[kPasses][4];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[p][e] = 0.f;
+  for (int q = 0; q < S.count; ++q) {
+    const void* src = parts[S.first_part + q];
+#pragma unroll
+    for (int p = 0; p < kPasses; ++p) {
+      const float4 v = load4(src, (i0 + lr0 + kRowsPerPass * p) * S.ld + j0 + lc, dtype);
+      acc[p][0] += v.x; acc[p][1] += v.y; acc[p][2] += v.z; acc[p][3] += v.w;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p)
+    store4(S.dst, (i0 + lr0 + kRowsPerPass * p) * S.ld + j0 + lc, dtype,
+           make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]));
+}
+
 }  // namespace
+
+hipError_t launch_gram_sum(const GramSum* sums_dev, int nsums, int64_t nblocks, const void* const* parts_dev,
+                           int32_t dtype, hipStream_t stream) {
+  if (nblocks <= 0 || nsums <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_sum_kernel, dim3(static_cast<unsigned>(nblocks)), dim3(kEwThreads), 0, stream,
+                     sums_dev, nsums, parts_dev, dtype);
+  return hipGetLastError();
+}
 
 hipError_t launch_momentum(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode, float mu,
                            int nesterov, float* partials, hipStream_t stream) {

@@ -38,6 +38,10 @@ struct EwMat {
   int32_t scale_idx;         // update/store: multiply O by scale[scale_idx] if >= 0
   int32_t aligned;           // all rows of src / mom / param are 16-byte aligned
   int32_t user_index;        // position in the caller's array (per-matrix outputs)
+  // shards of one tensor-parallel matrix: entries grp_first .. grp_first +
+  // grp_count - 1 share one norm (grp_count 0: a matrix of its own)
+  int32_t grp_first;
+  int32_t grp_count;
   int32_t pad_;
   int64_t blk_wide;          // first block of this matrix over wide tiles
   int64_t blk_stored;        // first block of this matrix over stored tiles
@@ -86,6 +90,22 @@ struct TileRef {
 constexpr int kNumXcd = 8;
 constexpr int kTileGroupRows = 4, kTileGroupCols = 4;
 
+// One sum of the partial Gram matrices of a sharded matrix (the stand-in
+// for their all-reduce across tensor-parallel ranks): dst = sum over
+// parts[first_part .. first_part + count - 1], each edge x edge with row
+// pitch ld, summed in fp32 in part order and rounded once.  edge is a
+// multiple of kEwTile; block b of the launch covers one kEwTile x kEwTile
+// tile of the entry whose blk_first is the last one <= b.
+struct GramSum {
+  void* dst;
+  int64_t ld;
+  int64_t blk_first;
+  int32_t edge;
+  int32_t first_part;
+  int32_t count;
+  int32_t pad_;
+};
+
 // One gradient of a clipping call.  The host orders the items by bucket, so
 // each bucket's blocks form one contiguous range.
 struct ClipItem {
@@ -114,6 +134,8 @@ hipError_t launch_finalize(const EwMat* mats_dev, int nmats, int64_t nblocks,
                            hipStream_t stream);
 
 // mode 0: W <- W*decay - lr_eff*o_scale*O in place; mode 1: out <- o_scale*O.
+hipError_t launch_gram_sum(const GramSum* sums_dev, int nsums, int64_t nblocks, const void* const* parts_dev,
+                           int32_t dtype, hipStream_t stream);
 hipError_t launch_update(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode,
                          const float* scale, hipStream_t stream);
 

@@ -241,3 +241,54 @@ def test_clip_argument_errors_before_launch(dm):
     dup[1].grad = dup[0].grad + 100
     assert call(dup, 2) == dm.DMUON_ERR_ALIASING
     assert call(ok, 0, ws=None, wsb=0) == dm.DMUON_OK                                    # nothing to do
+
+
+def test_sharded_argument_errors_before_launch(dm):
+    """Every argument check of the sharded entry point runs before anything
+    touches a device (fake device addresses are never dereferenced)."""
+    lib = dm._lib
+    h, _keep = dm._hparams()
+
+    def mats(specs, addr=1 << 42):
+        """specs: list of (split, [(rows, cols), ...])"""
+        shapes = [[rc for rc in sh] for _, sh in specs]
+        arr, keep = dm._sharded(shapes, [sp for sp, _ in specs])
+        for i, (_, sh) in enumerate(specs):
+            for j in range(len(sh)):
+                arr[i].shards[j].in_ = addr
+                arr[i].shards[j].out = addr
+                addr += 1 << 32
+        return arr, keep
+
+    def call(arr, n, ws=1 << 46, wsb=1 << 45, io=dm.DMUON_BF16):
+        return lib.dmuon_orthogonalize_sharded(arr, n, io, ctypes.byref(h), ws, wsb, None)
+
+    ok, k1 = mats([(1, [(256, 300), (256, 700)]), (0, [(100, 512), (412, 512)])])
+    need = lib.dmuon_orthogonalize_sharded_workspace_size(ok, 2, ctypes.byref(h))
+    assert need > 0
+    # one shard costs what the unsharded call costs, apart from the table
+    one, k2 = mats([(1, [(256, 1000)])])
+    rows, cols = (ctypes.c_int64 * 1)(256), (ctypes.c_int64 * 1)(1000)
+    assert abs(lib.dmuon_orthogonalize_sharded_workspace_size(one, 1, ctypes.byref(h)) -
+               lib.dmuon_orthogonalize_workspace_size(rows, cols, 1, ctypes.byref(h))) < 4096
+    assert call(ok, -1) == dm.DMUON_ERR_INVALID_ARG
+    bad, k3 = mats([(1, [(256, 300), (255, 700)])])          # d differs
+    assert call(bad, 1) == dm.DMUON_ERR_INVALID_ARG
+    assert "unsplit" in dm.dmuon_last_error()
+    bad, k4 = mats([(2, [(256, 300)])])                       # split
+    assert call(bad, 1) == dm.DMUON_ERR_INVALID_ARG
+    bad, k5 = mats([(1, [(256, 300)])])
+    bad[0].nshards = 0
+    assert call(bad, 1) == dm.DMUON_ERR_INVALID_ARG
+    bad, k6 = mats([(1, [(0, 300)])])
+    assert call(bad, 1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 2, io=7) == dm.DMUON_ERR_UNSUPPORTED
+    assert call(ok, 2, wsb=16) == dm.DMUON_ERR_WORKSPACE
+    assert call(ok, 2, ws=(1 << 46) + 8) == dm.DMUON_ERR_INVALID_ARG        # alignment
+    nul, k7 = mats([(1, [(256, 300)])])
+    nul[0].shards[0].out = None
+    assert call(nul, 1) == dm.DMUON_ERR_INVALID_ARG
+    dup, k8 = mats([(1, [(256, 300), (256, 700)])])
+    dup[0].shards[1].out = dup[0].shards[0].out
+    assert call(dup, 1) == dm.DMUON_ERR_ALIASING
+    assert call(ok, 0) == dm.DMUON_OK
