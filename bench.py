@@ -9,7 +9,13 @@ fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
                   [--ns-precision bf16] [--no-cpu-baseline] [--copy-probe]
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR      (writes the traffic summary)
   python bench.py --clip [--steps K] [--warmup W]        (gradient clipping alone)
+  python bench.py --tp 8 [--steps K] [--warmup W]        (NS on tensor-parallel shards)
   python bench.py --clip --pmc-summary FETCH_DIR WRITE_DIR
+
+--tp K times dmuon_orthogonalize_sharded with every matrix of the workload
+cut into K tensor-parallel shards as the usual layout cuts them (q, k, v,
+gate, up by output rows; o, down by input columns), and the unsharded
+dmuon_orthogonalize of the same matrices for comparison; one JSON line.
 
 --clip times dmuon_clip_grad_norm over the same gradient set (one bucket,
 p = 2, clipping active on every call: each call's max_norm is half the
@@ -64,6 +70,8 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
     ap.add_argument("--clip", action="store_true",
                     help="time gradient clipping of the workload's gradients instead of the step")
+    ap.add_argument("--tp", type=int, default=0,
+                    help="time NS on this many tensor-parallel shards per matrix instead of the step")
     return ap.parse_args()
 
 
@@ -223,6 +231,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.clip:
         return run_clip(args, dev)
+    if args.tp:
+        return run_tp(args, dev)
     w = di.workload(args.workload)
     hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
     shapes = [(m.rows, m.cols) for m in w.matrices]
@@ -440,6 +450,155 @@ def run_clip(args, dev):
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = clip_cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+TP_SPLIT = {"q_proj": 0, "k_proj": 0, "v_proj": 0, "gate_proj": 0, "up_proj": 0, "o_proj": 1, "down_proj": 1}
+TP_METRIC = ("NS TFLOP/s on tensor-parallel shards (Gram sums across shards) for a 3B-shaped owner set; "
+             "% bf16 MFMA peak")
+
+
+def tp_layout(w, k):
+    """(split, shard sizes) of every matrix: the usual tensor-parallel cut."""
+    out = []
+    for m in w.matrices:
+        split = TP_SPLIT[m.name.split(".")[-1]]
+        along = m.rows if split == 0 else m.cols
+        if along % k:
+            raise SystemExit(f"{m.name}: {along} does not split into {k} shards")
+        out.append((split, [along // k] * k))
+    return out
+
+
+def tp_cpu_baseline(w, k, hp, budget_s=60.0, min_s=10.0):
+    """The sharded oracle timed on this host: one matrix of each distinct
+    (shape, split), cheapest first, until ``min_s`` seconds are timed; the
+    other kinds are extrapolated by nominal flops; scaled to the workload by
+    counts."""
+    import dmuon_inputs as di
+    from oracle import tp_gram as otp
+    layout = tp_layout(w, k)
+    kinds = {}
+    for i, m in enumerate(w.matrices):
+        kinds.setdefault((m.rows, m.cols, layout[i][0]), []).append(i)
+    times = {}
+    t_start, timed = time.time(), 0.0
+    for key, idx in sorted(kinds.items(), key=lambda kv: nominal_flops([kv[0][:2]], hp["ns_steps"])):
+        i = idx[0]
+        _, u = di.grad_at(w, i, 0)
+        parts = otp.split_matrix(u, layout[i][0], layout[i][1])
+        t0 = time.perf_counter()
+        otp.orthogonalize_sharded(parts, layout[i][0], hp["ns_steps"], hp["ns_backend"])
+        dt = time.perf_counter() - t0
+        times[key] = dt
+        timed += dt
+        if timed >= min_s or time.time() - t_start > budget_s:
+            break
+    rate = sum(nominal_flops([s[:2]], hp["ns_steps"]) for s in times) / sum(times.values())
+    t_all = sum((times[s] if s in times else nominal_flops([s[:2]], hp["ns_steps"]) / rate) * len(idx)
+                for s, idx in kinds.items())
+    flops = nominal_flops([(m.rows, m.cols) for m in w.matrices], hp["ns_steps"])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": flops / t_all / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": (f"float64 numpy sharded oracle, one matrix of {len(times)} of the {len(kinds)} "
+                       f"(shape, split) kinds ({timed:.1f} s timed), the rest extrapolated by nominal "
+                       f"flops, scaled to {len(w.matrices)} matrices by counts")}
+
+
+def run_tp(args, dev):
+    """NS of the workload's matrices held as args.tp tensor-parallel shards,
+    one dmuon_orthogonalize_sharded call per step; the unsharded
+    dmuon_orthogonalize of the same matrices is timed alongside."""
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+
+    k = args.tp
+    w = di.workload(args.workload)
+    hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
+    nshp = {key: hp[key] for key in ("ns_steps", "ns_backend", "ns_precision")}
+    layout = tp_layout(w, k)
+    shapes = [(m.rows, m.cols) for m in w.matrices]
+    whole, ins, outs, splits = [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        u = torch.empty(r, c, dtype=torch.bfloat16, device=dev)
+        di.torch_normal_(u, 1.0, seed=300000 + i)
+        whole.append(u)
+        split, sizes = layout[i]
+        ins.append([p.contiguous() for p in torch.split(u, sizes, dim=1 if split == 1 else 0)])
+        outs.append([torch.empty_like(p) for p in ins[-1]])
+        splits.append(split)
+    ws_bytes = dm.dmuon_orthogonalize_sharded_workspace_size([[tuple(p.shape) for p in mat] for mat in ins],
+                                                            splits, **nshp)
+    ws_whole = dm.dmuon_orthogonalize_workspace_size(shapes, **nshp)
+    workspace = torch.empty(max(ws_bytes, ws_whole), dtype=torch.uint8, device=dev)
+    whole_out = [torch.empty_like(u) for u in whole]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    print(f"# {w.name}: {len(shapes)} matrices in {k} shards each, workspace {ws_bytes / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+
+    def timed(fn, steps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def sharded():
+        dm.dmuon_orthogonalize_sharded(ins, outs, splits, workspace=workspace, **nshp)
+
+    def unsharded():
+        dm.dmuon_orthogonalize(whole, whole_out, workspace=workspace, **nshp)
+
+    for _ in range(args.warmup):
+        sharded()
+        unsharded()
+    torch.cuda.synchronize()
+    ms_whole = timed(unsharded, max(1, args.steps // 2))
+    dm.dmuon_profile_begin()
+    ms_step = timed(sharded, args.steps)
+    prof = dm.dmuon_profile_end()["kernels"]
+    print(f"# sharded {ms_step:.3f} ms, unsharded {ms_whole:.3f} ms per call", file=sys.stderr, flush=True)
+
+    flops = nominal_flops(shapes, hp["ns_steps"])
+    peak = PEAK_BF16_TFLOPS if args.ns_precision == "bf16" else PEAK_F32_TFLOPS
+    gemm = {key: v for key, v in prof.items() if key.startswith("gemm")}
+    dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    kernels = {key: {"launches_per_step": v["launches"] / args.steps, "ms_per_step": v["ms"] / args.steps,
+                     "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
+                     "gbs": v["bytes"] / (v["ms"] * 1e-3) / 1e9}
+               for key, v in prof.items()}
+    out = {
+        "metric": TP_METRIC, "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": args.ns_precision,
+        "data": "synthetic (seeded normal matrices, generated on device, cut into shards)",
+        "config": {"workload": f"{w.name}, {k} tensor-parallel shards per matrix", "matrices": len(shapes),
+                   "shards": k * len(shapes), "elements": w.numel, "ns_backend": args.ns_backend,
+                   "ns_precision": args.ns_precision, "ns_steps": hp["ns_steps"],
+                   "splits": "q, k, v, gate, up: row blocks; o, down: column blocks"},
+        "unsharded_ms_per_call": ms_whole,
+        "unsharded_tflops_nominal": flops / (ms_whole * 1e-3) / 1e12,
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "traffic_unit": "HBM bytes per launch", "launches": dom["launches"],
+                     "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = tp_cpu_baseline(w, k, hp)
     print(json.dumps(out), flush=True)
 
 
