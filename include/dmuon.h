@@ -256,6 +256,40 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
                          const double* max_norm, double norm_type, double* total_norm,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Owner assignment (host only; FAQ, "Why isn't DMuon just ZeRO-1?": every
+ * dedicated matrix has one owner rank that runs its whole step; Training
+ * Guide, "Verify Parameter Assignment": the assignment is reported as loads
+ * per rank and an imbalance).  Each of the n matrices (rows[i] x cols[i],
+ * host arrays) gets a cost:
+ *   DMUON_COST_NUMEL       rows*cols
+ *   DMUON_COST_NS_NOMINAL  ns_steps*(4 m^2 n + 2 m^3), m = min, n = max
+ *   DMUON_COST_ROOFLINE    seconds at the device peaks: the flops of the
+ *                          products this library runs for the matrix (the
+ *                          form hp->ns_backend picks; symmetric results
+ *                          counted once) at 2516.6 TFLOP/s, plus 20 bytes per
+ *                          element (bf16 param and grad, fp32 momentum, the
+ *                          NS input and output) at 8 TB/s
+ * then matrices are taken in decreasing cost (ties: lower index first) and
+ * each goes to the least loaded rank (ties: lower rank).
+ *   hp         host, for ns_steps and ns_backend; NULL: 5 and gram
+ *   owner      host array of n ranks in 0..nranks-1 (required if n > 0)
+ *   cost       host array of n costs, or NULL
+ *   loads      host array of nranks summed costs, or NULL
+ *   imbalance  host, max(load)/mean(load) - 1 (0 with no cost), or NULL
+ * Returns INVALID_ARG for n < 0, nranks < 1, an unknown model or a shape
+ * outside 1..2^24; nothing is written then.
+ */
+typedef enum {
+  DMUON_COST_NUMEL = 0,
+  DMUON_COST_NS_NOMINAL = 1,
+  DMUON_COST_ROOFLINE = 2
+} dmuon_cost_model_t;
+
+int dmuon_assign_owners(const int64_t* rows, const int64_t* cols, int32_t n, int32_t nranks,
+                        int32_t cost_model, const dmuon_hparams_t* hp, int32_t* owner,
+                        double* cost, double* loads, double* imbalance);
+
 /* Readable name of a status code (static storage). */
 const char* dmuon_status_string(int status);
 

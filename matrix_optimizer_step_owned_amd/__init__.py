@@ -102,6 +102,9 @@ EXPORTS = {
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P,
                                             ctypes.c_size_t, _P]),
+    "dmuon_assign_owners": (ctypes.c_int, [_I64P, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _HP,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "dmuon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dmuon_last_error": (ctypes.c_char_p, []),
     "dmuon_backend_info": (ctypes.c_char_p, []),
@@ -379,6 +382,30 @@ def dmuon_orthogonalize_sharded(inputs: List[List[torch.Tensor]], outputs: List[
     _check(_lib.dmuon_orthogonalize_sharded(arr, n, dt, ctypes.byref(h),
                                             ws.data_ptr() if ws is not None else None, wsb,
                                             _stream(stream, dev)), "dmuon_orthogonalize_sharded")
+
+
+DMUON_COST_NUMEL = 0
+DMUON_COST_NS_NOMINAL = 1
+DMUON_COST_ROOFLINE = 2
+_COST_MODELS = {"numel": DMUON_COST_NUMEL, "ns_nominal": DMUON_COST_NS_NOMINAL, "roofline": DMUON_COST_ROOFLINE}
+
+
+def dmuon_assign_owners(shapes: Sequence[Sequence[int]], nranks: int, cost_model: str = "ns_nominal",
+                        **hp) -> dict:
+    """Owner rank of every matrix: {"owner", "cost", "loads", "imbalance"}."""
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(s[0]) for s in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(s[1]) for s in shapes])
+    owner = (ctypes.c_int32 * max(n, 1))()
+    cost = (ctypes.c_double * max(n, 1))()
+    loads = (ctypes.c_double * max(int(nranks), 1))()
+    imb = ctypes.c_double()
+    h, _keep = _hparams(**hp)
+    model = _COST_MODELS[cost_model] if isinstance(cost_model, str) else int(cost_model)
+    _check(_lib.dmuon_assign_owners(rows, cols, n, int(nranks), model, ctypes.byref(h), owner, cost, loads,
+                                    ctypes.byref(imb)), "dmuon_assign_owners")
+    return {"owner": list(owner)[:n], "cost": list(cost)[:n], "loads": list(loads)[:int(nranks)],
+            "imbalance": imb.value}
 
 
 def dmuon_apply_update(params: List[torch.Tensor], updates: List[torch.Tensor], *, lr: float = 0.02,

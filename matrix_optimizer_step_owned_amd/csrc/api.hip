@@ -875,6 +875,13 @@ std::string mat_name(const char* what, int i) { return std::string(what) + "[" +
 }  // namespace
 }  // namespace dmuon
 
+namespace dmuon {
+int set_last_error(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+}  // namespace dmuon
+
 using namespace dmuon;
 
 // ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <cstddef>
 #include <cstdint>
+#include <string>
 
 namespace dmuon {
 
@@ -120,6 +121,11 @@ struct ClipItem {
 constexpr int kClipThreads = 256;
 constexpr int kClipFinalizeThreads = 1024;
 constexpr int kClipChunkBytes = 65536;   // bytes of one gradient per block
+
+// Records msg as the calling thread's last error (dmuon_last_error) and
+// returns status; an empty message with no status clears it.
+int set_last_error(int status, const std::string& msg);
+inline void set_last_error(const char* msg) { set_last_error(0, msg); }
 
 // ---- launchers (each enqueues one kernel on `stream`) ----------------------
 
