@@ -10,12 +10,17 @@ fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
   python bench.py --pmc-summary FETCH_DIR WRITE_DIR      (writes the traffic summary)
   python bench.py --clip [--steps K] [--warmup W]        (gradient clipping alone)
   python bench.py --tp 8 [--steps K] [--warmup W]        (NS on tensor-parallel shards)
+  python bench.py --owners 8 [--steps K] [--warmup W]    (each owner's share of the step, timed)
   python bench.py --clip --pmc-summary FETCH_DIR WRITE_DIR
 
 --tp K times dmuon_orthogonalize_sharded with every matrix of the workload
 cut into K tensor-parallel shards as the usual layout cuts them (q, k, v,
 gate, up by output rows; o, down by input columns), and the unsharded
 dmuon_orthogonalize of the same matrices for comparison; one JSON line.
+
+--owners N plans the workload's matrices over N owners with each cost model
+of dmuon_assign_owners, runs every owner's share through dmuon_step on the
+one GPU, and reports the measured step-time imbalance of each plan.
 
 --clip times dmuon_clip_grad_norm over the same gradient set (one bucket,
 p = 2, clipping active on every call: each call's max_norm is half the
@@ -70,6 +75,8 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
     ap.add_argument("--clip", action="store_true",
                     help="time gradient clipping of the workload's gradients instead of the step")
+    ap.add_argument("--owners", type=int, default=0,
+                    help="time each owner's share of the step for this many owners")
     ap.add_argument("--tp", type=int, default=0,
                     help="time NS on this many tensor-parallel shards per matrix instead of the step")
     return ap.parse_args()
@@ -233,6 +240,8 @@ def main():
         return run_clip(args, dev)
     if args.tp:
         return run_tp(args, dev)
+    if args.owners:
+        return run_owners(args, dev)
     w = di.workload(args.workload)
     hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
     shapes = [(m.rows, m.cols) for m in w.matrices]
@@ -599,6 +608,111 @@ def run_tp(args, dev):
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = tp_cpu_baseline(w, k, hp)
+    print(json.dumps(out), flush=True)
+
+
+OWNERS_METRIC = "measured step-time imbalance of the owner shares (max / mean - 1) for a 3B-shaped model"
+
+
+def run_owners(args, dev):
+    """Plan the workload over args.owners owners with every cost model, run
+    each owner's share through dmuon_step, and compare the measured share
+    times: the imbalance the owners would see as waiting at the next
+    collective."""
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+    from oracle import owners as oow
+
+    N = args.owners
+    w = di.workload(args.workload)
+    hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
+    shapes = [(m.rows, m.cols) for m in w.matrices]
+    pdt = torch.bfloat16 if w.param_dtype == "bf16" else torch.float32
+    gdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
+    params, grads, moms = [], [], []
+    for i, (r, c) in enumerate(shapes):
+        p = torch.empty(r, c, dtype=pdt, device=dev)
+        di.torch_normal_(p, w.param_std, seed=1000 + i)
+        g = torch.empty(r, c, dtype=gdt, device=dev)
+        di.torch_normal_(g, w.grad_std, seed=100000 + i)
+        params.append(p)
+        grads.append(g)
+        moms.append(torch.zeros(r, c, dtype=torch.float32, device=dev))
+    plans = {}
+    t0 = time.perf_counter()
+    reps = 200
+    for _ in range(reps):
+        for model in ("numel", "ns_nominal", "roofline"):
+            plans[model] = dm.dmuon_assign_owners(shapes, N, model, ns_steps=hp["ns_steps"],
+                                                  ns_backend=hp["ns_backend"])
+    planner_us = (time.perf_counter() - t0) / (3 * reps) * 1e6
+    ws_need = 0
+    for model, pl in plans.items():
+        for q in range(N):
+            idx = [i for i, o in enumerate(pl["owner"]) if o == q]
+            if idx:
+                ws_need = max(ws_need, dm.dmuon_step_workspace_size([params[i] for i in idx], [grads[i] for i in idx],
+                                                                   [moms[i] for i in idx], **hp))
+    workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"# {w.name} over {N} owners; planner {planner_us:.1f} us per plan", file=sys.stderr, flush=True)
+
+    def share_ms(idx):
+        if not idx:
+            return 0.0
+        sub = ([params[i] for i in idx], [grads[i] for i in idx], [moms[i] for i in idx])
+        for _ in range(args.warmup):
+            dm.dmuon_step(*sub, workspace=workspace, **hp)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            dm.dmuon_step(*sub, workspace=workspace, **hp)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    dm.dmuon_profile_begin()
+    results = {}
+    for model, pl in plans.items():
+        ms = [share_ms([i for i, o in enumerate(pl["owner"]) if o == q]) for q in range(N)]
+        mean = sum(ms) / N
+        results[model] = {"predicted_imbalance": pl["imbalance"], "measured_imbalance": max(ms) / mean - 1,
+                          "share_ms": ms, "matrices_per_owner": [pl["owner"].count(q) for q in range(N)]}
+        print(f"# {model}: predicted {pl['imbalance']:.4f}, measured {max(ms) / mean - 1:.4f}, "
+              f"max share {max(ms):.2f} ms", file=sys.stderr, flush=True)
+    prof = dm.dmuon_profile_end()["kernels"]
+    gemm = {key: v for key, v in prof.items() if key.startswith("gemm")}
+    dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
+    peak = PEAK_BF16_TFLOPS if args.ns_precision == "bf16" else PEAK_F32_TFLOPS
+    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+    best = results["roofline"]
+    out = {
+        "metric": OWNERS_METRIC, "value": best["measured_imbalance"], "unit": "fraction",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": max(best["share_ms"]),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": args.ns_precision,
+        "data": "synthetic (seeded normal params and grads, generated on device)",
+        "config": {"workload": f"{w.name} over {N} owners", "matrices": len(shapes), "owners": N,
+                   "cost_model": "roofline", "ns_backend": args.ns_backend, "ns_precision": args.ns_precision},
+        "models": results, "planner_us_per_plan": planner_us,
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None, "traffic_unit": "HBM bytes per launch",
+                     "launches": dom["launches"], "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
+    }
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        n_plans = 0
+        while time.perf_counter() - t0 < 10.0:
+            oow.plan(shapes, N, "roofline", hp["ns_steps"], hp["ns_backend"])
+            n_plans += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n_plans / dt, "unit": "plans/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the pure-Python planner oracle on the {len(shapes)} shapes, "
+                                         f"{n_plans} plans in {dt:.1f} s (the library's planner: "
+                                         f"{1e6 / planner_us:.0f} plans/s)"}
     print(json.dumps(out), flush=True)
 
 
