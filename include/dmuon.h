@@ -257,6 +257,50 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * AdamW step of the symmetric (non-Muon) parameters (Training Guide, "Step 4:
+ * Create Optimizer": the optimizer's second group runs standard AdamW, with
+ * adamw_lr 1e-3, betas (0.9, 0.999), weight decay 0.01, eps 1e-8;
+ * "Semantic Param Groups": per-group values), fused over every tensor of a
+ * call.  For tensor i in group groups[tensors[i].group], at step t:
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p (1 - lr wd) - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ * (PyTorch's AdamW without amsgrad), evaluated in fp32 with the group's
+ * constants formed in fp64; a bf16 parameter is rounded once to nearest
+ * even.  m and v are fp32 and start at zero (the caller zeroes them).
+ *   tensors    host array of n descriptors; a NULL grad skips the tensor
+ *   groups     host array of ngroups hyperparameter sets
+ *   workspace  device, >= dmuon_adamw_workspace_size(n) bytes, 256-byte
+ *              aligned (the launch table)
+ * Errors (before any launch): INVALID_ARG for n < 0, ngroups < 1 with
+ * n > 0, a group with a non-finite lr, eps or weight decay, eps < 0, a beta
+ * outside [0, 1) or step < 1, a tensor with numel <= 0, a NULL param,
+ * exp_avg or exp_avg_sq, or a group index out of range; UNSUPPORTED for a
+ * dtype other than F32 or BF16; ALIASING when any two of the buffers
+ * overlap; WORKSPACE when the workspace is too small.
+ */
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+  int64_t step;          /* this call's step number, >= 1 */
+} dmuon_adamw_group_t;
+
+typedef struct {
+  int64_t numel;
+  void* param;           /* device, numel values of param_dtype, updated in place */
+  const void* grad;      /* device, numel values of grad_dtype; NULL: tensor skipped */
+  float* exp_avg;        /* device, numel fp32 (m), in/out */
+  float* exp_avg_sq;     /* device, numel fp32 (v), in/out */
+  int32_t param_dtype;   /* DMUON_F32 or DMUON_BF16 */
+  int32_t grad_dtype;    /* DMUON_F32 or DMUON_BF16 */
+  int32_t group;         /* index into groups */
+  int32_t pad_;
+} dmuon_adamw_tensor_t;
+
+size_t dmuon_adamw_workspace_size(int32_t n);
+int dmuon_adamw_step(const dmuon_adamw_tensor_t* tensors, int32_t n, const dmuon_adamw_group_t* groups,
+                     int32_t ngroups, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Owner assignment (host only; FAQ, "Why isn't DMuon just ZeRO-1?": every
  * dedicated matrix has one owner rank that runs its whole step; Training
  * Guide, "Verify Parameter Assignment": the assignment is reported as loads

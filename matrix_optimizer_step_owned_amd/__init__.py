@@ -74,6 +74,18 @@ class dmuon_sharded_t(ctypes.Structure):
                 ("split", ctypes.c_int32)]
 
 
+class dmuon_adamw_group_t(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", ctypes.c_int64)]
+
+
+class dmuon_adamw_tensor_t(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("param_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _I64P = ctypes.POINTER(ctypes.c_int64)
@@ -102,6 +114,10 @@ EXPORTS = {
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P,
                                             ctypes.c_size_t, _P]),
+    "dmuon_adamw_workspace_size": (ctypes.c_size_t, [ctypes.c_int32]),
+    "dmuon_adamw_step": (ctypes.c_int, [ctypes.POINTER(dmuon_adamw_tensor_t), ctypes.c_int32,
+                                        ctypes.POINTER(dmuon_adamw_group_t), ctypes.c_int32, _P, ctypes.c_size_t,
+                                        _P]),
     "dmuon_assign_owners": (ctypes.c_int, [_I64P, _I64P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _HP,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
@@ -382,6 +398,57 @@ def dmuon_orthogonalize_sharded(inputs: List[List[torch.Tensor]], outputs: List[
     _check(_lib.dmuon_orthogonalize_sharded(arr, n, dt, ctypes.byref(h),
                                             ws.data_ptr() if ws is not None else None, wsb,
                                             _stream(stream, dev)), "dmuon_orthogonalize_sharded")
+
+
+def dmuon_adamw_workspace_size(n: int) -> int:
+    return int(_lib.dmuon_adamw_workspace_size(int(n)))
+
+
+def dmuon_adamw_step(params: List[torch.Tensor], grads: List[Optional[torch.Tensor]], exp_avgs: List[torch.Tensor],
+                     exp_avg_sqs: List[torch.Tensor], *, step: int, lr: float = 1e-3, betas=(0.9, 0.999),
+                     eps: float = 1e-8, weight_decay: float = 0.01, groups: Optional[Sequence[dict]] = None,
+                     group_index: Optional[Sequence[int]] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """One fused AdamW step over every tensor (in place).  One hyperparameter
+    set from the keywords, or ``groups`` (dicts with lr, betas, eps,
+    weight_decay, step) with ``group_index`` naming each tensor's group."""
+    n = len(params)
+    if n == 0:
+        return
+    if groups is None:
+        groups = [dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay, step=step)]
+        group_index = [0] * n
+    if group_index is None or len(group_index) != n:
+        raise ValueError("group_index must name one group per tensor")
+    ga = (dmuon_adamw_group_t * len(groups))()
+    for k, g in enumerate(groups):
+        b1, b2 = g.get("betas", (0.9, 0.999))
+        ga[k].lr, ga[k].beta1, ga[k].beta2 = float(g.get("lr", 1e-3)), float(b1), float(b2)
+        ga[k].eps, ga[k].weight_decay = float(g.get("eps", 1e-8)), float(g.get("weight_decay", 0.01))
+        ga[k].step = int(g["step"])
+    ta = (dmuon_adamw_tensor_t * n)()
+    for i in range(n):
+        p, gr, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+        for t, what in ((p, "params"), (m, "exp_avgs"), (v, "exp_avg_sqs")):
+            if not t.is_contiguous():
+                raise ValueError(f"{what}[{i}] must be contiguous")
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError("exp_avg and exp_avg_sq must be float32")
+        if m.numel() != p.numel() or v.numel() != p.numel() or (gr is not None and gr.numel() != p.numel()):
+            raise ValueError(f"tensors[{i}]: sizes differ")
+        ta[i].numel = p.numel()
+        ta[i].param = p.data_ptr()
+        ta[i].grad = gr.data_ptr() if gr is not None else None
+        ta[i].exp_avg = m.data_ptr()
+        ta[i].exp_avg_sq = v.data_ptr()
+        ta[i].param_dtype = _dtype(p)
+        ta[i].grad_dtype = _dtype(gr) if gr is not None else _dtype(p)
+        ta[i].group = int(group_index[i])
+        if gr is not None and not gr.is_contiguous():
+            raise ValueError(f"grads[{i}] must be contiguous")
+    ws, wsb = _workspace(dmuon_adamw_workspace_size(n), params[0].device, workspace)
+    _check(_lib.dmuon_adamw_step(ta, n, ga, len(groups), ws.data_ptr() if ws is not None else None, wsb,
+                                 _stream(stream, params[0].device)), "dmuon_adamw_step")
 
 
 DMUON_COST_NUMEL = 0

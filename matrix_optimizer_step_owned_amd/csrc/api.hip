@@ -710,9 +710,10 @@ int check_device() {
 // ---------------------------------------------------------------------------
 
 enum ProfKind { PK_MOMENTUM, PK_FINALIZE, PK_GEMM_BF16, PK_GEMM_F32, PK_UPDATE,
-                PK_CLIP_NORM, PK_CLIP_FINALIZE, PK_CLIP_SCALE, PK_GRAM_SUM, PK_COUNT };
+                PK_CLIP_NORM, PK_CLIP_FINALIZE, PK_CLIP_SCALE, PK_GRAM_SUM, PK_ADAMW, PK_COUNT };
 const char* const kProfNames[PK_COUNT] = {"momentum", "finalize", "gemm_bf16", "gemm_f32", "update",
-                                          "clip_norm", "clip_finalize", "clip_scale", "gram_sum"};
+                                          "clip_norm", "clip_finalize", "clip_scale", "gram_sum",
+                                          "adamw"};
 
 struct ProfRec {
   int kind;
@@ -1518,6 +1519,95 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
   DMUON_HIP_TRY(prof_launch(PK_CLIP_SCALE, 0, 2 * bytes, stream, [&] {
     return launch_clip_scale(items_dev, n, L.blocks, coefs, stream);
   }));
+  return DMUON_OK;
+}
+
+// ---- dmuon_adamw_step --------------------------------------------------------
+
+size_t dmuon_adamw_workspace_size(int32_t n) { return n <= 0 ? 0 : align_up(sizeof(AdamItem) * size_t(n)); }
+
+int dmuon_adamw_step(const dmuon_adamw_tensor_t* tensors, int32_t n, const dmuon_adamw_group_t* groups,
+                     int32_t ngroups, void* workspace, size_t workspace_bytes, void* stream_) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return DMUON_OK;
+  if (!tensors) return fail(DMUON_ERR_INVALID_ARG, "tensors is NULL");
+  if (ngroups < 1 || !groups) return fail(DMUON_ERR_INVALID_ARG, "ngroups must be >= 1 and groups non-NULL");
+  for (int k = 0; k < ngroups; ++k) {
+    const dmuon_adamw_group_t& G = groups[k];
+    const std::string name = mat_name("groups", k);
+    if (!std::isfinite(G.lr) || !std::isfinite(G.weight_decay))
+      return fail(DMUON_ERR_INVALID_ARG, name + ": lr and weight_decay must be finite");
+    if (!std::isfinite(G.eps) || G.eps < 0) return fail(DMUON_ERR_INVALID_ARG, name + ": eps must be finite and >= 0");
+    if (!(G.beta1 >= 0 && G.beta1 < 1) || !(G.beta2 >= 0 && G.beta2 < 1))
+      return fail(DMUON_ERR_INVALID_ARG, name + ": betas must be in [0, 1)");
+    if (G.step < 1) return fail(DMUON_ERR_INVALID_ARG, name + ": step must be >= 1");
+  }
+  std::vector<int> active;
+  std::vector<Range> ranges;
+  for (int i = 0; i < n; ++i) {
+    const dmuon_adamw_tensor_t& T = tensors[i];
+    const std::string name = mat_name("tensors", i);
+    if (T.numel <= 0) return fail(DMUON_ERR_INVALID_ARG, name + ".numel must be > 0");
+    if (!T.param || !T.exp_avg || !T.exp_avg_sq)
+      return fail(DMUON_ERR_INVALID_ARG, name + ": param, exp_avg and exp_avg_sq must be non-NULL");
+    if (!dtype_ok(T.param_dtype) || !dtype_ok(T.grad_dtype))
+      return fail(DMUON_ERR_UNSUPPORTED, name + ": dtypes must be F32 or BF16");
+    if (T.group < 0 || T.group >= ngroups) return fail(DMUON_ERR_INVALID_ARG, name + ".group out of range");
+    if (!T.grad) continue;
+    active.push_back(i);
+    auto add = [&](const void* p, size_t bytes, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      ranges.push_back({lo, lo + bytes, name + "." + what});
+    };
+    const size_t ne = size_t(T.numel);
+    add(T.param, ne * dtype_size(T.param_dtype), "param");
+    add(T.grad, ne * dtype_size(T.grad_dtype), "grad");
+    add(T.exp_avg, ne * 4, "exp_avg");
+    add(T.exp_avg_sq, ne * 4, "exp_avg_sq");
+  }
+  if (active.empty()) return DMUON_OK;
+  const size_t need = align_up(sizeof(AdamItem) * active.size());
+  if (!workspace || workspace_bytes < need) return fail(DMUON_ERR_WORKSPACE, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  ranges.push_back({reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need,
+                    "workspace"});
+  int st = check_overlaps(ranges);
+  if (st) return st;
+  st = check_device();
+  if (st) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  int64_t blocks = 0, bytes = 0;
+  st = stage_table(workspace, need, stream, [&](char* host) {
+    AdamItem* items = reinterpret_cast<AdamItem*>(host);
+    for (size_t j = 0; j < active.size(); ++j) {
+      const dmuon_adamw_tensor_t& T = tensors[active[j]];
+      const dmuon_adamw_group_t& G = groups[T.group];
+      AdamItem& it = items[j];
+      it.p = T.param; it.g = T.grad; it.m = T.exp_avg; it.v = T.exp_avg_sq;
+      it.numel = T.numel;
+      it.blk_first = blocks;
+      const double t = static_cast<double>(G.step);
+      const double bc1 = 1.0 - std::pow(G.beta1, t), bc2 = 1.0 - std::pow(G.beta2, t);
+      it.decay = static_cast<float>(1.0 - G.lr * G.weight_decay);
+      it.step_size = static_cast<float>(G.lr / bc1);
+      it.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+      it.eps = static_cast<float>(G.eps);
+      it.beta1 = static_cast<float>(G.beta1);
+      it.one_minus_beta1 = static_cast<float>(1.0 - G.beta1);
+      it.beta2 = static_cast<float>(G.beta2);
+      it.one_minus_beta2 = static_cast<float>(1.0 - G.beta2);
+      it.p_dtype = T.param_dtype; it.g_dtype = T.grad_dtype;
+      it.aligned = aligned16(T.param) && aligned16(T.grad) && aligned16(T.exp_avg) && aligned16(T.exp_avg_sq);
+      blocks += (T.numel + kAdamChunk - 1) / kAdamChunk;
+      bytes += T.numel * (2 * int64_t(dtype_size(T.param_dtype)) + int64_t(dtype_size(T.grad_dtype)) + 16);
+    }
+  });
+  if (st) return st;
+  const AdamItem* items_dev = static_cast<const AdamItem*>(workspace);
+  const int na = static_cast<int>(active.size());
+  DMUON_HIP_TRY(prof_launch(PK_ADAMW, 0, bytes, stream, [&] { return launch_adamw(items_dev, na, blocks, stream); }));
   return DMUON_OK;
 }
 

@@ -122,6 +122,25 @@ constexpr int kClipThreads = 256;
 constexpr int kClipFinalizeThreads = 1024;
 constexpr int kClipChunkBytes = 65536;   // bytes of one gradient per block
 
+// One tensor of a fused AdamW call, with its group's constants folded:
+// decay = 1 - lr*wd, step_size = lr / (1 - beta1^t), inv_sqrt_bc2 =
+// 1 / sqrt(1 - beta2^t) (all formed in fp64 on the host, rounded to fp32).
+struct AdamItem {
+  void* p;
+  const void* g;
+  float* m;
+  float* v;
+  int64_t numel;
+  int64_t blk_first;     // first block of this tensor
+  float decay, step_size, inv_sqrt_bc2, eps;
+  float beta1, one_minus_beta1, beta2, one_minus_beta2;
+  int32_t p_dtype, g_dtype;
+  int32_t aligned;       // p, g, m and v all 16-byte aligned
+  int32_t pad_;
+};
+constexpr int kAdamThreads = 256;
+constexpr int kAdamChunk = 8192;   // elements of one tensor per block
+
 // Records msg as the calling thread's last error (dmuon_last_error) and
 // returns status; an empty message with no status clears it.
 int set_last_error(int status, const std::string& msg);
@@ -142,6 +161,7 @@ hipError_t launch_finalize(const EwMat* mats_dev, int nmats, int64_t nblocks,
 // mode 0: W <- W*decay - lr_eff*o_scale*O in place; mode 1: out <- o_scale*O.
 hipError_t launch_gram_sum(const GramSum* sums_dev, int nsums, int64_t nblocks, const void* const* parts_dev,
                            int32_t dtype, hipStream_t stream);
+hipError_t launch_adamw(const AdamItem* items_dev, int n, int64_t nblocks, hipStream_t stream);
 hipError_t launch_update(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode,
                          const float* scale, hipStream_t stream);
 

@@ -292,3 +292,54 @@ def test_sharded_argument_errors_before_launch(dm):
     dup[0].shards[1].out = dup[0].shards[0].out
     assert call(dup, 1) == dm.DMUON_ERR_ALIASING
     assert call(ok, 0) == dm.DMUON_OK
+
+
+def test_adamw_argument_errors_before_launch(dm):
+    """Every AdamW argument check runs before anything touches a device."""
+    lib = dm._lib
+    base = 1 << 43
+
+    def tensors(specs):
+        arr = (dm.dmuon_adamw_tensor_t * len(specs))()
+        for i, (numel, pdt, gdt, group) in enumerate(specs):
+            a = base + i * (1 << 34)
+            arr[i].numel, arr[i].param, arr[i].grad = numel, a, a + (1 << 32)
+            arr[i].exp_avg, arr[i].exp_avg_sq = a + (2 << 32), a + (3 << 32)
+            arr[i].param_dtype, arr[i].grad_dtype, arr[i].group = pdt, gdt, group
+        return arr
+
+    def groups(specs):
+        arr = (dm.dmuon_adamw_group_t * len(specs))()
+        for i, (lr, b1, b2, eps, wd, step) in enumerate(specs):
+            arr[i].lr, arr[i].beta1, arr[i].beta2, arr[i].eps, arr[i].weight_decay, arr[i].step = \
+                lr, b1, b2, eps, wd, step
+        return arr
+
+    good_g = groups([(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)])
+
+    def call(t, n, g=good_g, ng=1, ws=1 << 47, wsb=1 << 20):
+        return lib.dmuon_adamw_step(t, n, g, ng, ws, wsb, None)
+
+    ok = tensors([(1000, dm.DMUON_BF16, dm.DMUON_BF16, 0), (77, dm.DMUON_F32, dm.DMUON_F32, 0)])
+    assert dm.dmuon_adamw_workspace_size(2) >= 2 * 64 and dm.dmuon_adamw_workspace_size(0) == 0
+    assert call(ok, -1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 0) == dm.DMUON_OK
+    assert call(ok, 2, ng=0) == dm.DMUON_ERR_INVALID_ARG
+    for bad in ((float("nan"), 0.9, 0.999, 1e-8, 0.01, 1), (1e-3, 1.0, 0.999, 1e-8, 0.01, 1),
+                (1e-3, 0.9, -0.1, 1e-8, 0.01, 1), (1e-3, 0.9, 0.999, -1.0, 0.01, 1),
+                (1e-3, 0.9, 0.999, 1e-8, float("inf"), 1), (1e-3, 0.9, 0.999, 1e-8, 0.01, 0)):
+        assert call(ok, 2, g=groups([bad])) == dm.DMUON_ERR_INVALID_ARG, bad
+    assert call(tensors([(0, 1, 1, 0)]), 1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(tensors([(10, 1, 1, 1)]), 1) == dm.DMUON_ERR_INVALID_ARG          # group index
+    assert call(tensors([(10, 5, 1, 0)]), 1) == dm.DMUON_ERR_UNSUPPORTED
+    nul = tensors([(10, 1, 1, 0)])
+    nul[0].exp_avg = None
+    assert call(nul, 1) == dm.DMUON_ERR_INVALID_ARG
+    ali = tensors([(10, 1, 1, 0), (10, 1, 1, 0)])
+    ali[1].exp_avg_sq = ali[0].param
+    assert call(ali, 2) == dm.DMUON_ERR_ALIASING
+    assert call(ok, 2, wsb=16) == dm.DMUON_ERR_WORKSPACE
+    assert call(ok, 2, ws=(1 << 47) + 8) == dm.DMUON_ERR_INVALID_ARG
+    skip = tensors([(10, 1, 1, 0)])
+    skip[0].grad = None
+    assert call(skip, 1, ws=None, wsb=0) == dm.DMUON_OK                             # nothing to do
