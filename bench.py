@@ -11,6 +11,8 @@ fp32 momentum, bf16 NS products, Gram backend).  Prints one JSON line.
   python bench.py --clip [--steps K] [--warmup W]        (gradient clipping alone)
   python bench.py --tp 8 [--steps K] [--warmup W]        (NS on tensor-parallel shards)
   python bench.py --owners 8 [--steps K] [--warmup W]    (each owner's share of the step, timed)
+  python bench.py --adamw [--steps K] [--warmup W]       (fused AdamW of the symmetric parameters)
+  python bench.py --adamw --pmc-summary FETCH_DIR WRITE_DIR
   python bench.py --clip --pmc-summary FETCH_DIR WRITE_DIR
 
 --tp K times dmuon_orthogonalize_sharded with every matrix of the workload
@@ -21,6 +23,10 @@ dmuon_orthogonalize of the same matrices for comparison; one JSON line.
 --owners N plans the workload's matrices over N owners with each cost model
 of dmuon_assign_owners, runs every owner's share through dmuon_step on the
 one GPU, and reports the measured step-time imbalance of each plan.
+
+--adamw times dmuon_adamw_step over the AdamW group of a 3B-shaped model
+(the 128256 x 3072 embedding and 57 RMSNorm weights, bf16 parameters and
+gradients, fp32 moments); one JSON line, HBM-bound.
 
 --clip times dmuon_clip_grad_norm over the same gradient set (one bucket,
 p = 2, clipping active on every call: each call's max_norm is half the
@@ -49,6 +55,10 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_3b_stack_hbm_traffic
 GEMM_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "gemm.hip")
 CLIP_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "clip_scale_3b_stack_grads_hbm_traffic.md")
 CLIP_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "clip.hip")
+ADAMW_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_3b_symmetric_group_hbm_traffic.md")
+ADAMW_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "adamw.hip")
+ADAMW_METRIC = "fused AdamW GB/s (bf16 params and grads, fp32 moments) for a 3B-shaped symmetric group"
+ADAMW_SHAPES = [(128256, 3072)] + [(3072,)] * 57
 CLIP_METRIC = "gradient clipping GB/s (per-bucket global 2-norm clip, in place) for a 3B-shaped gradient set"
 COPY_PROBE_BYTES = 1 << 30
 
@@ -75,6 +85,8 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
     ap.add_argument("--clip", action="store_true",
                     help="time gradient clipping of the workload's gradients instead of the step")
+    ap.add_argument("--adamw", action="store_true",
+                    help="time the fused AdamW step of a 3B-shaped symmetric group instead of the step")
     ap.add_argument("--owners", type=int, default=0,
                     help="time each owner's share of the step for this many owners")
     ap.add_argument("--tp", type=int, default=0,
@@ -202,6 +214,18 @@ def cpu_baseline(w, hp, budget_s=30.0, min_s=10.0):
 
 def main():
     args = parse()
+    if args.pmc_summary and args.adamw:
+        r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], 1, kernel="adamw_kernel", per_step=1)
+        tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
+        print("# HBM traffic of adamw_kernel, the AdamW group of a 3B-shaped model (bf16 params and grads)\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            x = r[c]
+            print(f"- {c}: {x['kib_per_launch']:.6g} KiB per launch (the last timed call); "
+                  f"1 GiB copy reads {x['copy_kib']:.6g} KiB -> factor {x['factor']:.4f}; "
+                  f"{x['bytes_per_launch'] / 1e9:.4f} GB per launch")
+        print(f"- hbm_bytes_per_launch: {tot:.6e}")
+        print(f"- adamw_source_sha256: {source_sha256(ADAMW_SOURCE)}")
+        return
     if args.pmc_summary and args.clip:
         r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], 1, kernel="clip_scale_kernel", per_step=1)
         tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
@@ -242,6 +266,8 @@ def main():
         return run_tp(args, dev)
     if args.owners:
         return run_owners(args, dev)
+    if args.adamw:
+        return run_adamw(args, dev)
     w = di.workload(args.workload)
     hp = w.hparams(ns_backend=args.ns_backend, ns_precision=args.ns_precision)
     shapes = [(m.rows, m.cols) for m in w.matrices]
@@ -380,12 +406,8 @@ def clip_cpu_baseline(w, budget_s=60.0, min_s=10.0):
         done += 1
         if timed >= min_s or time.time() - t_start > budget_s:
             break
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": nbytes / timed / 1e9, "unit": "GB/s of bf16 gradient clipped", "cores": min(cores, threads),
+    # numpy's elementwise operations and reductions run on one thread
+    return {"value": nbytes / timed / 1e9, "unit": "GB/s of bf16 gradient clipped", "cores": 1,
             "kind": "oracle",
             "sample": (f"float64 numpy oracle, norm and scale of the first {done} gradients of the "
                        f"workload, one call each ({nbytes / 1e9:.3f} GB as bf16, {timed:.1f} s timed)")}
@@ -713,6 +735,100 @@ def run_owners(args, dev):
                                "sample": f"the pure-Python planner oracle on the {len(shapes)} shapes, "
                                          f"{n_plans} plans in {dt:.1f} s (the library's planner: "
                                          f"{1e6 / planner_us:.0f} plans/s)"}
+    print(json.dumps(out), flush=True)
+
+
+def adamw_cpu_baseline(budget_s=60.0, min_s=10.0):
+    """The AdamW oracle timed on this host on 2^22-element slices of the
+    group until ``min_s`` seconds are timed; parameter bytes (bf16) per
+    second over the algorithmic 22 bytes per element."""
+    import numpy as np
+    from oracle import adamw as oad
+    rng = np.random.default_rng(0)
+    n = 1 << 22
+    p = rng.standard_normal(n) * 0.02
+    g = rng.standard_normal(n) * 1e-3
+    m = np.zeros(n)
+    v = np.zeros(n)
+    t0 = time.time()
+    timed, done, step = 0.0, 0, 1
+    while timed < min_s and time.time() - t0 < budget_s:
+        s0 = time.perf_counter()
+        p_new, m, v = oad.adamw_step(p, g, m, v, step)
+        oad.store(p_new, "bf16")
+        timed += time.perf_counter() - s0
+        done += n
+        step += 1
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": done * 22 / timed / 1e9, "unit": "GB/s (22 bytes per element)", "cores": 1,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, {step - 1} steps of a 2^22-element slice "
+                      f"({done / 1e6:.0f} M elements, {timed:.1f} s timed; numpy elementwise, one thread of {cores})"}
+
+
+def run_adamw(args, dev):
+    """Fused AdamW over the symmetric group of a 3B-shaped model; a step is
+    one dmuon_adamw_step call over every tensor."""
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+
+    params, grads, ms, vs = [], [], [], []
+    for i, s in enumerate(ADAMW_SHAPES):
+        p = torch.empty(s, dtype=torch.bfloat16, device=dev)
+        di.torch_normal_(p, 0.02, seed=40000 + i)
+        g = torch.empty(s, dtype=torch.bfloat16, device=dev)
+        di.torch_normal_(g, 1e-3, seed=50000 + i)
+        params.append(p)
+        grads.append(g)
+        ms.append(torch.zeros(s, dtype=torch.float32, device=dev))
+        vs.append(torch.zeros(s, dtype=torch.float32, device=dev))
+    numel = sum(p.numel() for p in params)
+    alg_bytes = numel * 22
+    workspace = torch.empty(dm.dmuon_adamw_workspace_size(len(params)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    step = 1
+    for _ in range(args.warmup):
+        dm.dmuon_adamw_step(params, grads, ms, vs, step=step, workspace=workspace)
+        step += 1
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    dm.dmuon_profile_begin()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        dm.dmuon_adamw_step(params, grads, ms, vs, step=step, workspace=workspace)
+        step += 1
+    end.record(stream)
+    torch.cuda.synchronize()
+    prof = dm.dmuon_profile_end()["kernels"]
+    ms_step = start.elapsed_time(end) / args.steps
+    if args.copy_probe:
+        copy_probe(dev)
+    dom = prof["adamw"]
+    achieved = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+    out = {
+        "metric": ADAMW_METRIC, "value": alg_bytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (bf16 params and grads, fp32 moments)",
+        "data": "synthetic (seeded normal params and grads, generated on device)",
+        "config": {"workload": "3B AdamW group: 128256 x 3072 embedding + 57 RMSNorm weights of 3072",
+                   "tensors": len(params), "elements": numel, "alg_bytes_per_step": alg_bytes,
+                   "lr": 1e-3, "betas": [0.9, 0.999], "eps": 1e-8, "weight_decay": 0.01},
+        "elements_per_s": numel / (ms_step * 1e-3),
+        "roofline": {"bound": "hbm", "kernel": "adamw", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": read_traffic(ADAMW_TRAFFIC_SUMMARY, ADAMW_SOURCE),
+                     "traffic_unit": "HBM bytes per launch", "launches": dom["launches"],
+                     "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = adamw_cpu_baseline()
     print(json.dumps(out), flush=True)
 
 
