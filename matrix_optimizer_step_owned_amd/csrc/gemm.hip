@@ -17,17 +17,21 @@
 //
 // bf16 kernel: BT x BT output tiles (BT = 256 or 128), four waves in a 2 x 2
 // grid, each a (BT/2 x BT/2) block of v_mfma_f32_32x32x16_bf16 fragments with
-// fp32 accumulators.  Operands stream through a four-stage LDS ring, 32 k per
-// stage, filled by direct-to-LDS loads (global_load_lds_dwordx4: lane l of a
-// wave writes bytes 16l..16l+15 of a 1 KB LDS block).  LDS rows are 64 bytes
-// (four 16-byte chunks); chunk c of row r sits in slot c ^ (((r>>1)^(r>>2)) & 3),
-// which the loads realise by choosing each lane's source address, and which
-// makes the fragment reads (32 rows x one chunk per half-wave) bank-conflict
-// free for any 16 consecutive rows (the LDS serves 16 lanes of a 128-bit
-// read per cycle; a swizzle on bits 1..2 alone leaves rows r and r+8 in one
-// bank, which the bank-conflict counter shows).  Loads run two stages ahead of the multiplies; fragment reads for the
-// next half-stage are issued before the current half-stage's MFMAs, with one
-// barrier per stage placed between its two halves.
+// fp32 accumulators.  Operands stream through a two-slot LDS ring of 64-k
+// stages, filled by direct-to-LDS loads (global_load_lds_dwordx4: lane l of
+// a wave writes bytes 16l..16l+15 of a 1 KB LDS block).  An operand row of a
+// stage is 128 bytes, one cache line; chunk c of row r sits in slot
+// c ^ ((r >> 1) & 7), which the loads realise by choosing each lane's source
+// address, so that a fragment read (16 rows x one 16-byte chunk per cycle)
+// covers all 64 banks.  A stage runs as four k-quarters; each starts with an
+// MFMA and interleaves the next quarter's fragment reads with its MFMAs; the
+// one barrier per stage sits before the last quarter; the loads of the stage
+// two ahead are split between that last quarter and the next stage's first
+// one; the last two stages are peeled so that nothing is loaded past the end.
+// The epilogue stages the tile in the ring as bf16 and stores it row by row
+// (and column by column for a mirror or a transposed copy) in 16-byte pieces;
+// a diagonal tile of a symmetric product is made exactly symmetric in LDS
+// first.
 //
 // fp32 kernel (the fp32 NS mode): 64 x 64 x 16 tiles, four waves of 32 x 32,
 // v_mfma_f32_32x32x2f32, register-staged k-major LDS.
@@ -300,11 +304,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // next quarter's load; then one barrier, at which stage kt+1 has landed
   // (own loads counted, everyone's by the barrier) and every wave has
   // finished its LDS reads of stage kt; quarter 3 issues the reads of stage
-  // kt+1's first quarter and the first half of stage kt+2's loads into stage
-  // kt's slot, and quarter 0 of the next stage the second half, so that the
-  // loads' LDS writes spread over two quarters.  The loop is branch-free:
-  // past the last stage, loads re-fetch the last stage (in bounds, same
-  // bytes) and fragment reads re-read it, so the wait counts are constants.
+  // kt+1's first quarter and the first part of stage kt+2's loads into stage
+  // kt's slot, and quarter 0 of the next stage the rest, so that the loads'
+  // LDS writes spread over two quarters.  The wait counts are constants: the
+  // stage before the last issues no loads of a stage past the end, and the
+  // last stage issues none and has no barrier.
   static_assert(kStages == 2, "two-slot ring");
   // loads of a stage issued in quarter 3 (the rest go in the next quarter 0)
   constexpr int LQ3 = BT == 256 ? kLoadsEarly256 : LOADS / 2;
