@@ -143,6 +143,7 @@ struct Op {
   int32_t K, tiles_m, tiles_n, sym, alpha_pow, beta_pow, diag_limit;
   float alpha, beta, gamma;
   bool scaled;
+  bool last;              // the product that yields the matrix's O
 };
 
 // One sum of partial Gram matrices, run after the GEMM launches of `stage`.
@@ -353,6 +354,7 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
           u.beta = static_cast<float>(a);
           u.alpha_pow = u.beta_pow = (k == 0) ? 1 : 0;
           u.scaled = (k == 0);
+          u.last = k + 1 == K;
           upd.push_back(u);
         }
         st.push_back(upd);
@@ -381,7 +383,7 @@ void plan_ops(Plan& P, const Coeffs& cf, std::vector<std::vector<std::vector<Op>
       for (int i = f; i < e; ++i) {
         MatLayout& S = P.mats[i];
         Op o = left_op(i, S, qbuf[(K - 1) % 2], S.x0t, S.o, kNone);                                            // O = s Q X0
-        o.alpha_pow = 1; o.scaled = true;
+        o.alpha_pow = 1; o.scaled = true; o.last = true;
         fin.push_back(o);
         S.out = S.o;
       }
@@ -769,7 +771,15 @@ float lr_eff_of(double lr, int64_t rows, int64_t cols) {
   return static_cast<float>(lr * 0.2 * std::sqrt(static_cast<double>(std::max(rows, cols))));
 }
 
-void fill_tasks(const Plan& P, char* ws_base, GemmTask* out) {
+// Where the last product of a matrix updates its parameter instead of
+// leaving O in the workspace (dmuon_step with bf16 products).
+struct FusedUpdate {
+  void* param;
+  int32_t dtype;
+  float lr_eff, decay;
+};
+
+void fill_tasks(const Plan& P, char* ws_base, GemmTask* out, const FusedUpdate* fused = nullptr) {
   auto ptr = [&](size_t off) -> void* { return off == kNone ? nullptr : ws_base + off; };
   for (const Launch& l : P.launches) {
     for (int j = 0; j < l.count; ++j) {
@@ -785,6 +795,19 @@ void fill_tasks(const Plan& P, char* ws_base, GemmTask* out) {
       t.K = o.K; t.tiles_m = o.tiles_m; t.tiles_n = o.tiles_n; t.sym = o.sym;
       t.alpha_pow = o.alpha_pow; t.beta_pow = o.beta_pow; t.diag_limit = o.diag_limit;
       t.alpha = o.alpha; t.beta = o.beta; t.gamma = o.gamma;
+      if (fused && o.last) {
+        const MatLayout& L = P.mats[o.mat];
+        const FusedUpdate& f = fused[o.mat];
+        t.W = f.param;
+        t.ldw = L.cols;
+        t.w_m = static_cast<int32_t>(L.m);
+        t.w_n = static_cast<int32_t>(L.n);
+        t.w_dtype = f.dtype;
+        t.w_tall = L.tall ? 1 : 0;
+        t.w_vec = (L.cols % 8 == 0) && (reinterpret_cast<uintptr_t>(f.param) % 16 == 0);   // 8 bf16 = 16 bytes
+        t.lr_eff = f.lr_eff;
+        t.decay = f.decay;
+      }
     }
   }
   if (!P.tile_map.empty())
@@ -1001,6 +1024,16 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
   char* ws = static_cast<char*>(workspace);
   const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
   const float decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+  // with bf16 products and bf16 parameters the last product of each matrix
+  // updates the parameter itself (no O in the workspace, no separate update
+  // pass); a batch with any fp32 parameter takes the update pass
+  bool fuse_update = P.prec == DMUON_NS_PREC_BF16 && P.ns_steps > 0;
+  for (int j = 0; j < P.n && fuse_update; ++j) fuse_update = mats[active[j]].param_dtype == DT_BF16;
+  std::vector<FusedUpdate> fused(fuse_update ? P.n : 0);
+  for (size_t j = 0; j < fused.size(); ++j) {
+    const dmuon_matrix_t& m = mats[active[j]];
+    fused[j] = {m.param, m.param_dtype, lr_eff_of(hp->lr, m.rows, m.cols), decay};
+  }
   st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
     for (int j = 0; j < P.n; ++j) {
@@ -1020,7 +1053,7 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
       e.lr_eff = lr_eff_of(hp->lr, m.rows, m.cols);
       e.decay = decay;
     }
-    fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks));
+    fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks), fuse_update ? fused.data() : nullptr);
   });
   if (st) return st;
   const EwMat* em_dev = reinterpret_cast<const EwMat*>(ws + P.off_ewmats);
@@ -1046,6 +1079,7 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
   }));
   st = run_gemms(P, ws, stream);
   if (st) return st;
+  if (fuse_update) return DMUON_OK;
   DMUON_HIP_TRY(prof_launch(PK_UPDATE, 0, upd_bytes, stream, [&] {
     return launch_update(em_dev, P.n, P.blocks_stored, 0, scale, stream);
   }));

@@ -206,6 +206,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   const uint16_t* const Y = static_cast<const uint16_t*>(T.Y);
   const int64_t ldc = T.ldc, ldct = T.ldct, ldy = T.ldy;
   const int mode = T.sym ? (tm != tn ? 1 : 2) : (Ct ? 3 : 0);   // 0 plain, 1 mirror, 2 diagonal, 3 Ct
+  // fused parameter update (the last product of a step; mode 0, bf16 W)
+  uint16_t* const Wp = static_cast<uint16_t*>(T.W);
+  const int64_t ldw = T.ldw;
+  const int w_m = T.w_m, w_n = T.w_n, w_tall = T.w_tall, w_vec = T.w_vec;
+  const float lr_eff = T.lr_eff, w_decay = T.decay;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -429,6 +434,38 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   char* const stg = smem;
   const int t = threadIdx.x;
   const int h = lane >> 5;
+  constexpr int LPC = 2 * (BT / 8);              // lanes per column chunk of a block transpose
+  constexpr int NTQ = BT * BT * 2 / 64 / 256;    // block transposes per thread
+
+  // Fused parameter update (used at the end of the epilogue): a thread owns
+  // 8 * WNB pieces of 8 values of W; piece pc of batch k is W row r from
+  // column c on, taken from a staged tile row (wide W) or from a block
+  // transpose of the staged tile (tall W).
+  constexpr int NIT = BT * NCH / 256, WB = 8, QB = 2;
+  constexpr int WNB = NIT / WB;
+  static_assert(NIT % WB == 0 && NTQ % QB == 0 && NTQ / QB == WNB, "batches");
+  const int w_chunk = t % NCH;
+  const int64_t r_lim = w_tall ? w_n : w_m, c_lim = w_tall ? w_m : w_n;
+  auto piece = [&](int k, int pc, int64_t& r, int64_t& c) {
+    if (!w_tall) {
+      const int row = t / NCH + (256 / NCH) * (k * WB + pc);
+      r = int64_t(tm) * BT + row;
+      c = int64_t(tn) * BT + w_chunk * 8;
+    } else {
+      const int tq = t + 256 * (k * QB + pc / 4);
+      const int cc = tq / LPC, rb = (tq % LPC) >> 1, hf = tq & 1;
+      r = int64_t(tn) * BT + 8 * cc + 4 * hf + (pc & 3);   // W row = tile column
+      c = int64_t(tm) * BT + 8 * rb;                        // W columns = tile rows
+    }
+  };
+  auto load_batch = [&](int k, u32x4_t (&w)[WB]) {
+#pragma unroll
+    for (int pc = 0; pc < WB; ++pc) {
+      int64_t r, c;
+      piece(k, pc, r, c);
+      if (r < r_lim && c + 8 <= c_lim && w_vec) w[pc] = gload_u32x4(Wp + r * ldw + c);
+    }
+  };
 
   lds_barrier();                                 // every wave is done with the ring
   if (Y) {
@@ -495,8 +532,6 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // 8 x 4 block transposes: lane tq takes rows 8rb..8rb+7 of columns
   // 8cc + 4hf + 0..3 of the staged tile and returns, for sc = 0..3, tile
   // column 8cc + 4hf + sc over those 8 rows as one 16-byte piece
-  constexpr int LPC = 2 * (BT / 8);              // lanes per column chunk
-  constexpr int NTQ = BT * BT * 2 / 64 / 256;    // block transposes per thread
   auto transpose_block = [&](int tq, int& cc, int& rb, int& hf, u32x4_t (&o)[4]) {
     cc = tq / LPC;
     rb = (tq % LPC) >> 1;
@@ -547,6 +582,74 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       }
     }
     lds_barrier();
+  }
+
+  // The last product of a step: the tile is O (rounded to bf16, staged);
+  // instead of storing it, update the parameter: W <- W*decay - lr_eff*O in
+  // fp32, rounded once, in W's stored orientation (row pieces of the staged
+  // tile for a wide W, column pieces for a tall one).  Each thread owns
+  // 8 * WNB pieces of 8 values; all its W loads go out at once once the tile
+  // is staged (the accumulators are dead by then, so their registers are
+  // free), then the pieces are updated batch by batch; pieces past W's edge
+  // are skipped, and pieces at its edge (or on unaligned rows) go element by
+  // element.
+  if (Wp) {
+    // eight values: o and w bf16 pairs -> the updated bf16 pairs
+    auto update8 = [&](const u32x4_t& o, const u32x4_t& w) {
+      u32x4_t r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float a0 = fmaf(-lr_eff, __uint_as_float(o[k] << 16), __uint_as_float(w[k] << 16) * w_decay);
+        const float a1 = fmaf(-lr_eff, __uint_as_float(o[k] & 0xffff0000u),
+                              __uint_as_float(w[k] & 0xffff0000u) * w_decay);
+        r[k] = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+      }
+      return r;
+    };
+    // the first cnt (< 8, or unaligned) values of a piece, one by one
+    auto update_some = [&](const u32x4_t& o, uint16_t* wp, int cnt) {
+      for (int e = 0; e < cnt; ++e) {
+        const float of = __uint_as_float(((o[e >> 1] >> ((e & 1) * 16)) & 0xffffu) << 16);
+        wp[e] = static_cast<uint16_t>(f32_to_bf16_bits(fmaf(-lr_eff, of, bf16_bits_to_f32(wp[e]) * w_decay)));
+      }
+    };
+    auto run_batch = [&](int k, const u32x4_t (&w)[WB]) {
+      u32x4_t ov[WB];
+      if (!w_tall) {
+#pragma unroll
+        for (int pc = 0; pc < WB; ++pc) {
+          const int row = t / NCH + (256 / NCH) * (k * WB + pc);
+          ov[pc] = *reinterpret_cast<const u32x4_t*>(stg + row * ROWB + ((w_chunk ^ stg_swz(row)) << 4));
+        }
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < QB; ++qq) {
+          int cc, rb, hf;
+          u32x4_t o4[4];
+          transpose_block(t + 256 * (k * QB + qq), cc, rb, hf, o4);
+#pragma unroll
+          for (int sc = 0; sc < 4; ++sc) ov[qq * 4 + sc] = o4[sc];
+        }
+      }
+#pragma unroll
+      for (int pc = 0; pc < WB; ++pc) {
+        int64_t r, c;
+        piece(k, pc, r, c);
+        if (r >= r_lim || c >= c_lim) continue;
+        uint16_t* const wp = Wp + r * ldw + c;
+        if (c + 8 <= c_lim && w_vec) {
+          gstore_u32x4(wp, update8(ov[pc], w[pc]));
+        } else {
+          update_some(ov[pc], wp, static_cast<int>(c + 8 <= c_lim ? 8 : c_lim - c));
+        }
+      }
+    };
+    u32x4_t wall[WNB][WB];
+#pragma unroll
+    for (int k = 0; k < WNB; ++k) load_batch(k, wall[k]);
+#pragma unroll
+    for (int k = 0; k < WNB; ++k) run_batch(k, wall[k]);
+    return;
   }
 
   // C, row by row: thread t covers chunk t % NCH of rows t / NCH + (256 / NCH) k

@@ -60,6 +60,12 @@ struct EwMat {
 //        the upper triangle is also written mirrored, so C is exactly
 //        symmetric.
 //   Ct:  if not null, C^T is also written there (N x M, ldct).
+//   W:   if not null (the last product of a matrix in a step, bf16 kernel
+//        and bf16 parameters only), C is not written; instead the parameter
+//        is updated in place, W <- W*decay - lr_eff*O with O the product
+//        rounded to bf16, evaluated in fp32 and rounded once to bf16.  W is rows x cols of the wide
+//        orientation (w_m x w_n valid), or its transpose when w_tall; ldw is
+//        its row pitch; w_vec: 16-byte accesses along W rows are aligned.
 struct GemmTask {
   const void* A;
   const void* B;
@@ -67,13 +73,16 @@ struct GemmTask {
   void* Ct;
   const void* Y;
   const float* scale;
-  int64_t lda, ldb, ldc, ldct, ldy;
+  void* W;
+  int64_t lda, ldb, ldc, ldct, ldy, ldw;
   int32_t K;
   int32_t tiles_m, tiles_n;
   int32_t sym;
   int32_t alpha_pow, beta_pow;
   int32_t diag_limit;
+  int32_t w_m, w_n, w_dtype, w_tall, w_vec;
   float alpha, beta, gamma;
+  float lr_eff, decay;
 };
 
 // One block of a grouped GEMM launch: which task and which output tile.
