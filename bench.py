@@ -413,6 +413,65 @@ def clip_cpu_baseline(w, budget_s=60.0, min_s=10.0):
                        f"workload, one call each ({nbytes / 1e9:.3f} GB as bf16, {timed:.1f} s timed)")}
 
 
+def clip_then_step(w, grads, dev, stream, norm, reps=3):
+    """Clipping followed by the step over the same matrices, two ways: the
+    in-place clip then dmuon_step, and the clip's coefficients then
+    dmuon_step with the gradients scaled as the momentum pass reads them.
+    Every call clips (max_norm is half the gradients' current norm).
+    Returns ms per (clip + step) for both."""
+    import torch
+    import dmuon_inputs as di
+    import matrix_optimizer_step_owned_amd as dm
+    hp = w.hparams()
+    params, moms = [], []
+    for i, m in enumerate(w.matrices):
+        p = torch.empty(m.rows, m.cols, dtype=torch.bfloat16, device=dev)
+        di.torch_normal_(p, w.param_std, seed=1000 + i)
+        params.append(p)
+        moms.append(torch.zeros(m.rows, m.cols, dtype=torch.float32, device=dev))
+    ws = torch.empty(dm.dmuon_step_workspace_size(params, grads, moms, **hp), dtype=torch.uint8, device=dev)
+    cws = torch.empty(max(1, dm._lib.dmuon_clip_workspace_size(*_clip_args(dm, grads), 1)), dtype=torch.uint8,
+                      device=dev)
+    coefs = torch.ones(1, dtype=torch.float64, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    state = {"norm": norm}
+
+    def unfused():
+        state["norm"] *= 0.5
+        dm.dmuon_clip_grad_norm(grads, state["norm"], workspace=cws)
+        dm.dmuon_step(params, grads, moms, workspace=ws, **hp)
+
+    def fused():
+        dm.dmuon_clip_coefficients(grads, 0.5 * state["norm"], coefs=coefs, workspace=cws)
+        dm.dmuon_step(params, grads, moms, workspace=ws, grad_scale=coefs, **hp)
+
+    t_unfused = timed(unfused)
+    t_fused = timed(fused)
+    del ws
+    return {"in_place_clip_then_step_ms": t_unfused, "coefficients_then_scaled_step_ms": t_fused,
+            "saved_ms": t_unfused - t_fused}
+
+
+def _clip_args(dm, grads):
+    import ctypes
+    arr = (dm.dmuon_grad_t * len(grads))()
+    for i, g in enumerate(grads):
+        arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = g.numel(), g.data_ptr(), dm._dtype(g), 0
+    return arr, len(grads)
+
+
 def run_clip(args, dev):
     """Gradient clipping alone: dmuon_clip_grad_norm over the workload's
     gradient set; a step is one call (norm, finalize, scale)."""
@@ -454,6 +513,7 @@ def run_clip(args, dev):
     ms_step = start.elapsed_time(end) / args.steps
     if args.copy_probe:
         copy_probe(dev)
+    fused = None if args.copy_probe else clip_then_step(w, grads, dev, stream, norm)
     # every call wrote: the scale kernel ran on every gradient
     alg_bytes = 3 * nbytes
     value = alg_bytes / (ms_step * 1e-3) / 1e9
@@ -471,6 +531,7 @@ def run_clip(args, dev):
                    "grad_dtype": w.grad_dtype, "norm_type": 2, "buckets": 1,
                    "alg_bytes_per_call": alg_bytes},
         "kernels": kernels,
+        "clip_then_step": fused,
         "roofline": {"bound": "hbm", "kernel": "clip_scale", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": read_traffic(CLIP_TRAFFIC_SUMMARY, CLIP_SOURCE),

@@ -122,6 +122,26 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dmuon_step with the gradient clipping of the Training Guide ("Gradient
+ * Clipping": the dedicated gradients are clipped after their reduce and
+ * before momentum and Newton-Schulz) folded into the momentum pass: matrix
+ * i's gradient is read as g * (*grad_scale[i]), the fp64 product rounded
+ * once to the gradient's dtype -- the values dmuon_clip_grad_norm would
+ * have written in place -- so that dmuon_clip_coefficients followed by this
+ * call gives the bit-identical parameters and momenta of dmuon_clip_grad_norm
+ * followed by dmuon_step, without the clip's read-and-write pass over the
+ * gradients.  The gradients themselves are not modified.
+ *   grad_scale  host array of n pointers, each to one double in device
+ *               memory (e.g. into dmuon_clip_coefficients' coef_out), or
+ *               NULL for a matrix that is not scaled; the array itself must
+ *               not be NULL when n > 0
+ * Everything else as dmuon_step (same workspace size).
+ */
+int dmuon_step_scaled(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                      const double* const* grad_scale, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * The momentum stage alone (the Hyperparameter Guide's momentum and nesterov
  * rows): updates every matrix's momentum buffer in place and writes the NS
  * input U of matrix i to ns_input[i] (device), dense and row-major in the wide
@@ -255,6 +275,18 @@ size_t dmuon_clip_workspace_size(const dmuon_grad_t* grads, int32_t n, int32_t n
 int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
                          const double* max_norm, double norm_type, double* total_norm,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The clip's norms and coefficients without the scaling pass: coef_out
+ * (device, nbuckets doubles, required) receives coef_b; the gradients are
+ * only read.  For dmuon_step_scaled.  Arguments, workspace and errors as
+ * dmuon_clip_grad_norm (coef_out must not overlap the other buffers);
+ * n == 0 writes nothing.
+ */
+int dmuon_clip_coefficients(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
+                            const double* max_norm, double norm_type, double* total_norm,
+                            double* coef_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * AdamW step of the symmetric (non-Muon) parameters (Training Guide, "Step 4:

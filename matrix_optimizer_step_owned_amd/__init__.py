@@ -96,6 +96,7 @@ EXPORTS = {
     "dmuon_hparams_default": (None, [_HP]),
     "dmuon_step_workspace_size": (ctypes.c_size_t, [_MP, ctypes.c_int32, _HP]),
     "dmuon_step": (ctypes.c_int, [_MP, ctypes.c_int32, _HP, _P, ctypes.c_size_t, _P]),
+    "dmuon_step_scaled": (ctypes.c_int, [_MP, ctypes.c_int32, _HP, _PP, _P, ctypes.c_size_t, _P]),
     "dmuon_momentum_workspace_size": (ctypes.c_size_t, [_MP, ctypes.c_int32]),
     "dmuon_momentum": (ctypes.c_int, [_MP, ctypes.c_int32, _HP, _PP, ctypes.c_int32, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -114,6 +115,9 @@ EXPORTS = {
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P,
                                             ctypes.c_size_t, _P]),
+    "dmuon_clip_coefficients": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
     "dmuon_adamw_workspace_size": (ctypes.c_size_t, [ctypes.c_int32]),
     "dmuon_adamw_step": (ctypes.c_int, [ctypes.POINTER(dmuon_adamw_tensor_t), ctypes.c_int32,
                                         ctypes.POINTER(dmuon_adamw_group_t), ctypes.c_int32, _P, ctypes.c_size_t,
@@ -264,8 +268,13 @@ def dmuon_step_workspace_size(params, grads, momenta=None, **hp) -> int:
 
 def dmuon_step(params: List[torch.Tensor], grads: List[Optional[torch.Tensor]],
                momenta: List[torch.Tensor], *, workspace: Optional[torch.Tensor] = None,
-               stream=None, **hp) -> None:
-    """One Muon step over a batch of owned matrices (in place on params and momenta)."""
+               stream=None, grad_scale: Optional[torch.Tensor] = None,
+               grad_scale_index: Optional[Sequence[int]] = None, **hp) -> None:
+    """One Muon step over a batch of owned matrices (in place on params and
+    momenta).  With ``grad_scale`` (a float64 device tensor of clipping
+    coefficients, e.g. from dmuon_clip_coefficients) matrix i's gradient is
+    scaled by grad_scale[grad_scale_index[i]] as it is read
+    (dmuon_step_scaled); an index of -1 leaves that matrix unscaled."""
     n = len(params)
     if n == 0:
         return
@@ -273,8 +282,19 @@ def dmuon_step(params: List[torch.Tensor], grads: List[Optional[torch.Tensor]],
     h, _keep = _hparams(**hp)
     nbytes = int(_lib.dmuon_step_workspace_size(mats, n, ctypes.byref(h)))
     ws, wsb = _workspace(nbytes, params[0].device, workspace)
-    _check(_lib.dmuon_step(mats, n, ctypes.byref(h), ws.data_ptr() if ws is not None else None, wsb,
-                           _stream(stream, params[0].device)), "dmuon_step")
+    wsp = ws.data_ptr() if ws is not None else None
+    st = _stream(stream, params[0].device)
+    if grad_scale is None:
+        _check(_lib.dmuon_step(mats, n, ctypes.byref(h), wsp, wsb, st), "dmuon_step")
+        return
+    if grad_scale.dtype != torch.float64 or not grad_scale.is_contiguous():
+        raise TypeError("grad_scale must be a contiguous float64 tensor")
+    idx = list(grad_scale_index) if grad_scale_index is not None else [0] * n
+    if len(idx) != n or any(k >= grad_scale.numel() for k in idx):
+        raise ValueError("grad_scale_index must give one index into grad_scale per matrix")
+    base = grad_scale.data_ptr()
+    ptrs = (ctypes.c_void_p * n)(*[base + 8 * int(k) if k >= 0 else None for k in idx])
+    _check(_lib.dmuon_step_scaled(mats, n, ctypes.byref(h), ptrs, wsp, wsb, st), "dmuon_step_scaled")
 
 
 def dmuon_momentum_workspace_size(grads, momenta) -> int:
@@ -533,6 +553,41 @@ def dmuon_clip_grad_norm(grads: List[torch.Tensor], max_norm, *, norm_type: floa
                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream, device)),
            "dmuon_clip_grad_norm")
     return total_norm
+
+
+def dmuon_clip_coefficients(grads: List[torch.Tensor], max_norm, *, norm_type: float = 2.0,
+                            buckets: Optional[Sequence[int]] = None, total_norm: Optional[torch.Tensor] = None,
+                            coefs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Per-bucket clipping coefficients (float64, on the device) without
+    scaling the gradients; for dmuon_step(..., grad_scale=...)."""
+    n = len(grads)
+    if buckets is None:
+        buckets = [0] * n
+    nb = (max(buckets) + 1) if n else 1
+    if isinstance(max_norm, (int, float)):
+        max_norm = [float(max_norm)] * nb
+    nb = max(nb, len(max_norm))
+    if len(max_norm) != nb or len(buckets) != n:
+        raise ValueError("one max_norm per bucket and one bucket per gradient")
+    arr = (dmuon_grad_t * max(n, 1))()
+    for i, g in enumerate(grads):
+        if not g.is_contiguous():
+            raise ValueError(f"grads[{i}] must be contiguous")
+        arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = g.numel(), g.data_ptr(), _dtype(g), int(buckets[i])
+    device = grads[0].device if n else torch.device("cpu")
+    if coefs is None:
+        coefs = torch.ones(nb, dtype=torch.float64, device=device)
+    if n == 0:
+        return coefs
+    mx = (ctypes.c_double * nb)(*[float(v) for v in max_norm])
+    nbytes = int(_lib.dmuon_clip_workspace_size(arr, n, nb))
+    ws, wsb = _workspace(nbytes, device, workspace)
+    _check(_lib.dmuon_clip_coefficients(arr, n, nb, mx, float(norm_type),
+                                        total_norm.data_ptr() if total_norm is not None else None,
+                                        coefs.data_ptr(), ws.data_ptr() if ws is not None else None, wsb,
+                                        _stream(stream, device)), "dmuon_clip_coefficients")
+    return coefs
 
 
 def dmuon_plan_describe(shapes: Sequence[Sequence[int]], **hp) -> dict:

@@ -984,8 +984,8 @@ size_t dmuon_step_workspace_size(const dmuon_matrix_t* mats, int32_t n, const dm
   return active.empty() ? 0 : plan->ws_bytes;
 }
 
-int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp, void* workspace,
-               size_t workspace_bytes, void* stream_) {
+static int step_impl(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                     const double* const* grad_scale, void* workspace, size_t workspace_bytes, void* stream_) {
   g_last_error.clear();
   Coeffs cf;
   std::vector<int> active;
@@ -1052,6 +1052,7 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
       e.blk_wide = P.blk_wide[j]; e.blk_stored = P.blk_stored[j];
       e.lr_eff = lr_eff_of(hp->lr, m.rows, m.cols);
       e.decay = decay;
+      e.gscale = grad_scale ? grad_scale[active[j]] : nullptr;
     }
     fill_tasks(P, ws, reinterpret_cast<GemmTask*>(host + P.off_tasks), fuse_update ? fused.data() : nullptr);
   });
@@ -1084,6 +1085,20 @@ int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
     return launch_update(em_dev, P.n, P.blocks_stored, 0, scale, stream);
   }));
   return DMUON_OK;
+}
+
+int dmuon_step(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return step_impl(mats, n, hp, nullptr, workspace, workspace_bytes, stream);
+}
+
+int dmuon_step_scaled(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t* hp,
+                      const double* const* grad_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n > 0 && !grad_scale) {
+    g_last_error = "grad_scale is NULL";
+    return DMUON_ERR_INVALID_ARG;
+  }
+  return step_impl(mats, n, hp, grad_scale, workspace, workspace_bytes, stream);
 }
 
 // ---- dmuon_momentum --------------------------------------------------------
@@ -1474,9 +1489,9 @@ size_t dmuon_clip_workspace_size(const dmuon_grad_t* grads, int32_t n, int32_t n
   return clip_layout(grads, n, nbuckets).total;
 }
 
-int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
-                         double norm_type, double* total_norm, void* workspace, size_t workspace_bytes,
-                         void* stream_) {
+static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                     double norm_type, double* total_norm, double* coef_out, void* workspace,
+                     size_t workspace_bytes, void* stream_) {
   g_last_error.clear();
   if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
   if (nbuckets <= 0) return fail(DMUON_ERR_INVALID_ARG, "nbuckets must be >= 1");
@@ -1507,6 +1522,9 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
   if (total_norm)
     ranges.push_back({reinterpret_cast<uintptr_t>(total_norm),
                       reinterpret_cast<uintptr_t>(total_norm) + sizeof(double) * size_t(nbuckets), "total_norm"});
+  if (coef_out)
+    ranges.push_back({reinterpret_cast<uintptr_t>(coef_out),
+                      reinterpret_cast<uintptr_t>(coef_out) + sizeof(double) * size_t(nbuckets), "coef_out"});
   int st = check_overlaps(ranges);
   if (st) return st;
   st = check_device();
@@ -1539,7 +1557,7 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
   if (st) return st;
   const ClipItem* items_dev = reinterpret_cast<const ClipItem*>(ws + L.off_items);
   double* partials = reinterpret_cast<double*>(ws + L.off_partials);
-  double* coefs = reinterpret_cast<double*>(ws + L.off_coefs);
+  double* coefs = coef_out ? coef_out : reinterpret_cast<double*>(ws + L.off_coefs);
   int64_t bytes = 0;
   for (int i = 0; i < n; ++i) bytes += grads[i].numel * int64_t(dtype_size(grads[i].dtype));
   DMUON_HIP_TRY(prof_launch(PK_CLIP_NORM, 0, bytes, stream, [&] {
@@ -1550,10 +1568,29 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
                                 reinterpret_cast<const double*>(ws + L.off_max_norm), partials, norm_type,
                                 total_norm, coefs, stream);
   }));
+  if (coef_out) return DMUON_OK;   // the coefficients are the result; nothing is scaled
   DMUON_HIP_TRY(prof_launch(PK_CLIP_SCALE, 0, 2 * bytes, stream, [&] {
     return launch_clip_scale(items_dev, n, L.blocks, coefs, stream);
   }));
   return DMUON_OK;
+}
+
+int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                         double norm_type, double* total_norm, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return clip_impl(grads, n, nbuckets, max_norm, norm_type, total_norm, nullptr, workspace, workspace_bytes,
+                   stream);
+}
+
+int dmuon_clip_coefficients(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                            double norm_type, double* total_norm, double* coef_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!coef_out) {
+    g_last_error = "coef_out is NULL";
+    return DMUON_ERR_INVALID_ARG;
+  }
+  return clip_impl(grads, n, nbuckets, max_norm, norm_type, total_norm, coef_out, workspace, workspace_bytes,
+                   stream);
 }
 
 // ---- dmuon_adamw_step --------------------------------------------------------

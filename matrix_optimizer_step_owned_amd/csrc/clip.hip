@@ -34,24 +34,11 @@ __device__ __forceinline__ void st16(void* p, u32x4_t v) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp64 -> fp32 rounded to odd: truncate, then set the last bit when inexact.
-// A value rounded to odd at 24 bits and then to nearest-even at 8 bits is the
-// nearest-even rounding of the fp64 value itself (24 >= 2 * 8 + 2), so the
-// bf16 result is rounded once from the fp64 product.
-__device__ __forceinline__ float f64_to_f32_odd(double d) {
-  const float f = static_cast<float>(d);
-  const double back = static_cast<double>(f);
-  if (back == d) return f;
-  uint32_t u = __float_as_uint(f);
-  if (fabs(back) > fabs(d)) u -= 1;   // rounded away from zero: step back toward it
-  return __uint_as_float(u | 1u);
-}
-
 // two fp64 products -> packed bf16 pair, each rounded once to nearest-even
 __device__ __forceinline__ uint32_t pack2_from_f64(double a, double b) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t v = {f64_to_f32_odd(a), f64_to_f32_odd(b)};
+  const f32x2_t v = {f64_to_f32_round_odd(a), f64_to_f32_round_odd(b)};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 

@@ -59,6 +59,14 @@ __device__ __forceinline__ void store4(void* p, int64_t i, int dt, float4 v) {
   }
 }
 
+// A gradient value scaled as gradient clipping writes it: the fp64 product,
+// rounded once to the gradient's dtype.
+__device__ __forceinline__ float scale_grad(float g, double c, int dt) {
+  const double d = static_cast<double>(g) * c;
+  if (dt == DT_F32) return static_cast<float>(d);
+  return bf16_bits_to_f32(f32_to_bf16_bits(f64_to_f32_round_odd(d)));
+}
+
 __device__ __forceinline__ float get(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
@@ -101,12 +109,18 @@ momentum_kernel(const EwMat* __restrict__ mats, int nmats, int mode, float mu, i
   float u[kPasses][4];
   float ss = 0.f;
   const bool full = M.aligned && r0 + kEwTile <= M.rows && c0 + kEwTile <= M.cols;
+  const double gsc = M.gscale ? *M.gscale : 1.0;   // clipping coefficient, if fused
+  const bool scaled = gsc != 1.0;
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     const int64_t r = r0 + lr0 + kRowsPerPass * p;
     const int64_t base = r * M.cols + c0 + lc;
     if (full) {
-      const float4 g = load4(M.src, base, M.src_dtype);
+      float4 g = load4(M.src, base, M.src_dtype);
+      if (scaled) {
+        g.x = scale_grad(g.x, gsc, M.src_dtype); g.y = scale_grad(g.y, gsc, M.src_dtype);
+        g.z = scale_grad(g.z, gsc, M.src_dtype); g.w = scale_grad(g.w, gsc, M.src_dtype);
+      }
       float4 uu;
       if (mode == 0) {
         const float4 m = *reinterpret_cast<const float4*>(M.mom + base);
@@ -131,7 +145,8 @@ momentum_kernel(const EwMat* __restrict__ mats, int nmats, int mode, float mu, i
         float v = 0.f;
         if (r < M.rows && c < M.cols) {
           const int64_t idx = r * M.cols + c;
-          const float g = load1(M.src, idx, M.src_dtype);
+          float g = load1(M.src, idx, M.src_dtype);
+          if (scaled) g = scale_grad(g, gsc, M.src_dtype);
           if (mode == 0) {
             const float mn = fmaf(mu, M.mom[idx], g);
             M.mom[idx] = mn;

@@ -28,6 +28,9 @@ struct EwMat {
   void* u_dst;               // momentum/load: U destination (wide), or null
   void* u_dst_t;             // momentum/load: U^T destination (wide_cols x wide_rows), or null
   const void* o_src;         // update/store: O source (wide)
+  const double* gscale;      // momentum: if not null, the gradient is first
+                             // scaled by *gscale (fp64 product rounded once to
+                             // src_dtype, as gradient clipping writes it)
   int64_t ld_wide;           // leading dimension of the wide buffers (elements)
   int64_t ld_wide_t;         // leading dimension of the U^T buffer
   int32_t wide_rows;         // rows of the wide region to write (>= m; zero fill)
@@ -149,6 +152,19 @@ struct AdamItem {
 };
 constexpr int kAdamThreads = 256;
 constexpr int kAdamChunk = 8192;   // elements of one tensor per block
+
+// fp64 -> fp32 rounded to odd: truncate, then set the last bit when inexact.
+// A value rounded to odd at 24 bits and then to nearest-even at 8 bits is the
+// nearest-even rounding of the fp64 value itself (24 >= 2 * 8 + 2), so a bf16
+// result formed this way is rounded once from the fp64 value.
+__device__ __forceinline__ float f64_to_f32_round_odd(double d) {
+  const float f = static_cast<float>(d);
+  const double back = static_cast<double>(f);
+  if (back == d) return f;
+  uint32_t u = __float_as_uint(f);
+  if (fabs(back) > fabs(d)) u -= 1;   // rounded away from zero: step back toward it
+  return __uint_as_float(u | 1u);
+}
 
 // Records msg as the calling thread's last error (dmuon_last_error) and
 // returns status; an empty message with no status clears it.

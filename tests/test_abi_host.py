@@ -343,3 +343,17 @@ def test_adamw_argument_errors_before_launch(dm):
     skip = tensors([(10, 1, 1, 0)])
     skip[0].grad = None
     assert call(skip, 1, ws=None, wsb=0) == dm.DMUON_OK                             # nothing to do
+
+
+def test_fused_clip_entry_points_reject_null(dm):
+    lib = dm._lib
+    h, _keep = dm._hparams()
+    mats = _mats(dm, [(256, 512)])
+    assert lib.dmuon_step_scaled(mats, 1, ctypes.byref(h), None, 1 << 40, 1 << 40, None) == dm.DMUON_ERR_INVALID_ARG
+    assert "grad_scale" in dm.dmuon_last_error()
+    arr = (dm.dmuon_grad_t * 1)()
+    arr[0].numel, arr[0].grad, arr[0].dtype, arr[0].bucket = 100, 1 << 41, dm.DMUON_BF16, 0
+    mx = (ctypes.c_double * 1)(1.0)
+    assert lib.dmuon_clip_coefficients(arr, 1, 1, mx, 2.0, None, None, 1 << 42, 1 << 20, None) == \
+        dm.DMUON_ERR_INVALID_ARG
+    assert "coef_out" in dm.dmuon_last_error()

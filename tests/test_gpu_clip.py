@@ -138,3 +138,45 @@ def test_clip_full_3b_stack(lib):
         assert abs(r - coef) <= 1e-3 * coef, (i, r, coef)      # bf16 rounding of every element
     for i in sample:
         _check_values(f64(grads[i]), before[i] * coef, "bf16", f"matrix {i}")
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_clip_fused_into_step_is_bitwise_equal(lib, gdt):
+    """dmuon_clip_coefficients + dmuon_step with grad_scale gives the same
+    parameters and momenta, bit for bit, as dmuon_clip_grad_norm (in place)
+    + dmuon_step, and leaves the gradients untouched; two clipped buckets, a
+    bucket that does not clip and a matrix left unscaled (index -1, in a
+    bucket whose coefficient is 1)."""
+    shapes = [(256, 512), (1000, 1500), (130, 70), (2048, 128), (384, 384), (70, 130)]
+    buckets = [0, 0, 1, 1, 2, 2]
+    pdt = "bf16"
+    params_a, params_b, moms_a, moms_b, grads = [], [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        raw, _ = di.normal_matrix(r, c, 0.02, pdt, seed=0, tag=(90, i))
+        params_a.append(upload(raw, pdt))
+        params_b.append(upload(raw, pdt))
+        graw, _ = di.normal_matrix(r, c, 1e-2 * (i + 1), gdt, seed=0, tag=(91, i))
+        grads.append(upload(graw, gdt))
+        moms_a.append(torch.zeros(r, c, dtype=torch.float32, device=DEV))
+        moms_b.append(torch.zeros(r, c, dtype=torch.float32, device=DEV))
+    totals = lib.dmuon_clip_grad_norm([g.clone() for g in grads], [1e30] * 3, buckets=buckets)
+    torch.cuda.synchronize()
+    t = totals.cpu().numpy()
+    max_norm = [0.3 * t[0], 0.5 * t[1], 2.0 * t[2]]
+    grads_a = [g.clone() for g in grads]
+    grads_b = [g.clone() for g in grads]
+    ta = lib.dmuon_clip_grad_norm(grads_a, max_norm, buckets=buckets)
+    lib.dmuon_step(params_a, grads_a, moms_a)
+    tb = torch.empty(3, dtype=torch.float64, device=DEV)
+    coefs = lib.dmuon_clip_coefficients(grads_b, max_norm, buckets=buckets, total_norm=tb)
+    index = list(buckets)
+    index[5] = -1
+    lib.dmuon_step(params_b, grads_b, moms_b, grad_scale=coefs, grad_scale_index=index)
+    torch.cuda.synchronize()
+    c = coefs.cpu().numpy()
+    assert c[0] < 1.0 and c[1] < 1.0 and c[2] == 1.0
+    assert torch.equal(ta, tb)
+    for i in range(len(shapes)):
+        assert torch.equal(grads_b[i], grads[i]), i
+        assert torch.equal(moms_a[i], moms_b[i]), i
+        assert torch.equal(params_a[i], params_b[i]), i
