@@ -28,6 +28,9 @@
 // one barrier per stage sits before the last quarter; the loads of the stage
 // two ahead are split between that last quarter and the next stage's first
 // one; the last two stages are peeled so that nothing is loaded past the end.
+// A diagonal tile of a product of a matrix with itself (A A, X X^T) loads its
+// rows once: the B fragments are read from the A rows (a second instance of
+// the loop, chosen per block).
 // The epilogue stages the tile in the ring as bf16 and stores it row by row
 // (and column by column for a mirror or a transposed copy) in 16-byte pieces;
 // a diagonal tile of a symmetric product is made exactly symmetric in LDS
@@ -261,14 +264,15 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
                                        (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
   };
-  auto read_frags = [&](int s, int kq, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F]) {
+  auto read_frags = [&](int s, int kq, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F], auto same) {
+    constexpr int BOFF = decltype(same)::value ? 0 : OPB;
     const char* st = smem + (s % kStages) * STB + frag_off[kq];
 #pragma unroll
     for (int i = 0; i < F; ++i)
       fa[i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * WT + i * 32) * kRowBytes);
 #pragma unroll
     for (int j = 0; j < F; ++j)
-      fb[j] = *reinterpret_cast<const bf16x8_t*>(st + OPB + (wn * WT + j * 32) * kRowBytes);
+      fb[j] = *reinterpret_cast<const bf16x8_t*>(st + BOFF + (wn * WT + j * 32) * kRowBytes);
   };
   auto mfmas = [&](const bf16x8_t (&fa)[F], const bf16x8_t (&fb)[F]) {
 #pragma unroll
@@ -290,8 +294,8 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   bf16x8_t fa0[F], fb0[F], fa1[F], fb1[F];
   // one k-quarter: MFMAs on (fa, fb) while the next quarter's fragments load
   auto quarter = [&](int s, int kq_next, bf16x8_t (&na)[F], bf16x8_t (&nb)[F],
-                     const bf16x8_t (&fa)[F], const bf16x8_t (&fb)[F]) {
-    read_frags(s, kq_next, na, nb);
+                     const bf16x8_t (&fa)[F], const bf16x8_t (&fb)[F], auto same) {
+    read_frags(s, kq_next, na, nb, same);
     mfmas(fa, fb);
     // the reads go out two per MFMA over the first NFRAG/2 MFMAs, as early
     // as possible behind the first one
@@ -370,35 +374,42 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
                             : (NMFMA == 4 && NFRAG == 4), "schedule");
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto main_loop = [&](auto same) {
+  constexpr bool kSame = decltype(same)::value;
   issue_part(0, 0, 0);
-  issue_part(0, 0, 1);
+  if constexpr (!kSame) issue_part(0, 0, 1);
   issue_part(nk > 1 ? 1 : 0, 1, 0);
   wait_vmcnt<LQ3>();
   __builtin_amdgcn_s_barrier();
-  read_frags(0, 0, fa0, fb0);
+  read_frags(0, 0, fa0, fb0, same);
   // One stage.  kLast: the last stage (no loads, no reads of a next stage,
   // no barrier); kNoAhead: the stage before it (no stage kt+2 to load).
   auto stage_step = [&](int kt, auto last, auto no_ahead) {
     constexpr bool kLast = decltype(last)::value, kNoAhead = decltype(no_ahead)::value;
     if constexpr (kLast) {
-      quarter(kt, 1, fa1, fb1, fa0, fb0);
-      quarter(kt, 2, fa0, fb0, fa1, fb1);
-      quarter(kt, 3, fa1, fb1, fa0, fb0);
+      quarter(kt, 1, fa1, fb1, fa0, fb0, same);
+      quarter(kt, 2, fa0, fb0, fa1, fb1, same);
+      quarter(kt, 3, fa1, fb1, fa0, fb0, same);
       mfmas(fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
     } else {
       // quarter 0, with the rest of stage kt+1's loads
-      read_frags(kt, 1, fa1, fb1);
-      issue_part(kt + 1, kt + 1, 1);
-      mfmas(fa0, fb0);
-      pin_quarter_with_loads(std::integral_constant<int, LQ0>{});
-      quarter(kt, 2, fa0, fb0, fa1, fb1);
-      quarter(kt, 3, fa1, fb1, fa0, fb0);
+      read_frags(kt, 1, fa1, fb1, same);
+      if constexpr (kSame) {
+        mfmas(fa0, fb0);
+        pin_quarter_with_loads(std::integral_constant<int, 0>{});
+      } else {
+        issue_part(kt + 1, kt + 1, 1);
+        mfmas(fa0, fb0);
+        pin_quarter_with_loads(std::integral_constant<int, LQ0>{});
+      }
+      quarter(kt, 2, fa0, fb0, fa1, fb1, same);
+      quarter(kt, 3, fa1, fb1, fa0, fb0, same);
       wait_vmcnt<0>();
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // quarter 3, with the first part of stage kt+2's loads
-      read_frags(kt + 1, 0, fa0, fb0);
+      read_frags(kt + 1, 0, fa0, fb0, same);
       if constexpr (kNoAhead) {
         mfmas(fa1, fb1);
         pin_quarter_with_loads(std::integral_constant<int, 0>{});
@@ -413,6 +424,12 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   for (; kt + 2 < nk; ++kt) stage_step(kt, std::false_type{}, std::false_type{});
   if (kt + 1 < nk) stage_step(kt++, std::false_type{}, std::true_type{});
   stage_step(kt, std::true_type{}, std::false_type{});
+  };
+  // a diagonal tile of a matrix times itself: one operand's rows serve both
+  if (T.A == T.B && tm == tn)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
 
