@@ -83,6 +83,8 @@ def parse():
                     help="after the timed steps, copy 1 GiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
+                    help="summarise a rocprofv3 run of MFMA counters (one step) against a bench line and exit")
     ap.add_argument("--clip", action="store_true",
                     help="time gradient clipping of the workload's gradients instead of the step")
     ap.add_argument("--adamw", action="store_true",
@@ -129,6 +131,33 @@ def pmc_summary(fetch_dir, write_dir, steps, kernel="gemm_bf16_kernel", per_step
         res[counter] = {"kib_per_launch": sum(last) / len(last), "copy_kib": copy_kib, "factor": factor,
                         "bytes_per_launch": sum(last) / len(last) * 1024.0 * factor, "launches": len(last)}
     return res
+
+
+def mfma_summary(pmc_dir, bench_json, per_step=16):
+    """Executed MFMA work of the GEMM launches of one step from
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (x 512 flops), and the MFMA-busy and
+    shader-busy cycle counters, against the algorithmic flops and the GEMM
+    time of a bench line."""
+    rows = {}
+    for counter in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES"):
+        vals = sorted((di, v) for k, di, v in _pmc_rows(pmc_dir, counter) if "gemm_bf16_kernel" in k)
+        rows[counter] = [v for _, v in vals[-per_step:]]
+    with open(bench_json) as f:
+        b = json.loads(f.read().strip().splitlines()[-1])
+    exec_flops = sum(rows["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
+    alg_flops = b["kernels"]["gemm_bf16"]["tflops"] * 1e12 * b["ns_ms_per_step"] * 1e-3
+    t = b["ns_ms_per_step"] * 1e-3
+    print("# Executed MFMA work of gemm_bf16_kernel, 3B 28-layer stack (workload 2), gram, bf16\n")
+    print(f"- executed MFMA flops per step (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, {per_step} launches): "
+          f"{exec_flops / 1e12:.2f} TFLOP")
+    print(f"- algorithmic flops per step (symmetric results counted once): {alg_flops / 1e12:.2f} TFLOP "
+          f"(executed / algorithmic = {exec_flops / alg_flops:.3f})")
+    print(f"- GEMM time per step (bench HIP events): {t * 1e3:.2f} ms -> executed MFMA rate "
+          f"{exec_flops / t / 1e12:.1f} TFLOP/s = {exec_flops / t / 1e12 / PEAK_BF16_TFLOPS:.3f} of {PEAK_BF16_TFLOPS}")
+    busy = sum(rows["SQ_VALU_MFMA_BUSY_CYCLES"])
+    sq = sum(rows["SQ_BUSY_CYCLES"])
+    print(f"- SQ_VALU_MFMA_BUSY_CYCLES summed: {busy:.4e}; SQ_BUSY_CYCLES summed: {sq:.4e}")
+    print(f"- gemm_source_sha256: {source_sha256()}")
 
 
 def read_traffic(summary=TRAFFIC_SUMMARY, source=GEMM_SOURCE):
@@ -214,6 +243,8 @@ def cpu_baseline(w, hp, budget_s=30.0, min_s=10.0):
 
 def main():
     args = parse()
+    if args.mfma_summary:
+        return mfma_summary(*args.mfma_summary)
     if args.pmc_summary and args.adamw:
         r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], 1, kernel="adamw_kernel", per_step=1)
         tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
