@@ -183,6 +183,24 @@ def nominal_flops(shapes, ns_steps):
     return tot
 
 
+def step_roofline(w, gemm_flops, ms_step, peak_tflops):
+    """The step rate against its roofline: the GEMM launches' algorithmic
+    flops at the matrix-core peak and the elementwise passes' algorithmic
+    bytes (grad in, fp32 momentum in and out, the NS input out, parameter in
+    and out, O in: 12 + 6 bytes per element with bf16 parameters and
+    gradients) at the HBM peak, overlapped (max) or in sequence (sum).
+    Steps/s and matrices/s share these fractions."""
+    pb = 2 if w.param_dtype == "bf16" else 4
+    gb = 2 if w.grad_dtype == "bf16" else 4
+    ew_bytes = w.numel * (gb + 8 + 2 + 2 * pb + 2)
+    t_mfma = gemm_flops / (peak_tflops * 1e12) * 1e3
+    t_hbm = ew_bytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    overlap, seq = max(t_mfma, t_hbm), t_mfma + t_hbm
+    return {"gemm_ms_at_peak": t_mfma, "elementwise_ms_at_peak": t_hbm, "elementwise_bytes": ew_bytes,
+            "overlap_bound_ms": overlap, "sequential_bound_ms": seq,
+            "frac_of_overlap_bound": overlap / ms_step, "frac_of_sequential_bound": seq / ms_step}
+
+
 def cpu_baseline(w, hp, budget_s=30.0, min_s=10.0):
     """The oracle timed on this host: one step of one matrix of each distinct
     shape (inputs from the seeded generator), repeated over further matrices
@@ -389,6 +407,7 @@ def main():
                    "grad_dtype": w.grad_dtype, "momentum_dtype": "f32"},
         "steps_per_s": 1e3 / ms_step,
         "matrices_per_s": len(shapes) * 1e3 / ms_step,
+        "step_roofline": step_roofline(w, exec_flops, ms_step, peak),
         "ns_tflops_nominal": flops_step / (ns_ms * 1e-3) / 1e12,
         "ns_executed_tflops": exec_flops / (ns_ms * 1e-3) / 1e12,
         "ns_executed_frac_of_peak": exec_flops / (ns_ms * 1e-3) / 1e12 / peak,
