@@ -205,16 +205,19 @@ std::shared_ptr<Plan> build_plan(const std::vector<ShapeSpec>& shapes, const std
   P->prec = prec;
   P->ns_steps = with_ns ? static_cast<int>(cf.abc.size() / 3) : 0;
   // Tile edge: fp32 products use 64.  bf16 products use 256 x 256 tiles
-  // (half the LDS traffic per flop of 128 x 128) when the batch is big
-  // enough to keep every CU busy with them -- at least four waves of such
-  // tiles in the first (X X^T) stage -- and 128 otherwise; matrices narrower
-  // than 256 always use 128.
-  int64_t big_tiles = 0;
+  // (half the LDS traffic per flop of 128 x 128) when the first (X X^T)
+  // stage has at least half a wave of them and most of them come from wide
+  // matrices (measured: a single 4096^2 matrix, 136 such tiles, runs 12 %
+  // faster with them; sixteen 1024^2 matrices, 160 tiles of short K, 8 %
+  // slower), and 128 otherwise; matrices narrower than 256 always use 128.
+  int64_t big_tiles = 0, big_tiles_wide = 0;
   for (const ShapeSpec& s : shapes) {
-    const int64_t t = ((s.tall ? s.cols : s.rows) + kTileBf16Big - 1) / kTileBf16Big;
+    const int64_t m = s.tall ? s.cols : s.rows;
+    const int64_t t = (m + kTileBf16Big - 1) / kTileBf16Big;
     big_tiles += t * (t + 1) / 2;
+    if (m >= kBigTileMinDim) big_tiles_wide += t * (t + 1) / 2;
   }
-  bool use_big = prec == DMUON_NS_PREC_BF16 && big_tiles >= kBigTileMinCount;
+  bool use_big = prec == DMUON_NS_PREC_BF16 && big_tiles >= kBigTileMinCount && 2 * big_tiles_wide >= big_tiles;
   if (prec == DMUON_NS_PREC_BF16 && tile_override != 0) use_big = tile_override == kTileBf16Big;
   P->tile = prec == DMUON_NS_PREC_BF16 ? (use_big ? kTileBf16Big : kTileBf16) : kTileF32;
   P->blk_wide.resize(n);

@@ -211,7 +211,9 @@ hipError_t launch_clip_scale(const ClipItem* items_dev, int n, int64_t nblocks, 
 constexpr int kTileBf16 = 128;
 constexpr int kTileBf16Big = 256;
 constexpr int kTileF32 = 64;
-// 256-tiles are used when the first NS stage has at least this many of them.
-constexpr int64_t kBigTileMinCount = 1024;
+// 256-tiles are used when the first NS stage has at least this many of them
+// and at least half of them belong to matrices kBigTileMinDim or more wide.
+constexpr int64_t kBigTileMinCount = 128;
+constexpr int64_t kBigTileMinDim = 2048;
 
 }  // namespace dmuon

@@ -180,8 +180,13 @@ def test_plan_tile_choice(dm):
     assert all(m["m_pad"] % 256 == 0 and m["n_pad"] % 256 == 0 for m in big["matrices"])
     # the 196 matrices still form one launch per stage and operand form
     assert len(big["launches"]) == 16 and big["launches"][0]["tasks"] == 196
-    small = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(1).matrices])
-    assert small["tile"] == 128
+    # one 3B layer: 410 such tiles, mostly of 3072-wide matrices
+    layer = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(1).matrices])
+    assert layer["tile"] == 256
+    # too few 256-tiles, or mostly narrow matrices: 128
+    assert dm.dmuon_plan_describe([(3072, 8192)])["tile"] == 128
+    assert dm.dmuon_plan_describe([(1024, 1024)] * 16)["tile"] == 128
+    assert dm.dmuon_plan_describe([(4096, 4096)])["tile"] == 256
     # in a big batch, matrices narrower than 256 keep 128-tiles in launches of their own
     mixed = dm.dmuon_plan_describe([(m.rows, m.cols) for m in di.workload(2).matrices] + [(128, 2048)])
     assert mixed["matrices"][-1]["tile"] == 128 and mixed["matrices"][-1]["m_pad"] == 128
