@@ -43,6 +43,9 @@ int fail(int status, const std::string& msg) {
 constexpr double kDefaultCoeffs[3] = {3.4445, -4.7750, 2.0315};
 constexpr int kMaxNsSteps = 16;
 constexpr int64_t kMaxDim = int64_t(1) << 22;   // tile coordinates are 16-bit
+// the GEMM kernel's operand descriptors span 255 rows of the padded leading
+// dimension plus one stage (and per-lane byte offsets are 32-bit)
+static_assert(255 * kMaxDim * 2 + 128 < (int64_t(1) << 31), "operand descriptor range");
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }

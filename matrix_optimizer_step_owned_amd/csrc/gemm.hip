@@ -18,8 +18,10 @@
 // bf16 kernel: BT x BT output tiles (BT = 256 or 128), four waves in a 2 x 2
 // grid, each a (BT/2 x BT/2) block of v_mfma_f32_32x32x16_bf16 fragments with
 // fp32 accumulators.  Operands stream through a two-slot LDS ring of 64-k
-// stages, filled by direct-to-LDS loads (global_load_lds_dwordx4: lane l of
-// a wave writes bytes 16l..16l+15 of a 1 KB LDS block).  An operand row of a
+// stages, filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds:
+// lane l of a wave writes bytes 16l..16l+15 of a 1 KB LDS block; the base
+// is a per-operand descriptor in scalar registers, the per-lane offsets are
+// fixed).  An operand row of a
 // stage is 128 bytes, one cache line; chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7), which the loads realise by choosing each lane's source
 // address, so that a fragment read (16 rows x one 16-byte chunk per cycle)
@@ -32,9 +34,9 @@
 // rows once: the B fragments are read from the A rows (a second instance of
 // the loop, chosen per block).
 // The epilogue stages the tile in the ring as bf16 and stores it row by row
-// (and column by column for a mirror or a transposed copy) in 16-byte pieces;
-// a diagonal tile of a symmetric product is made exactly symmetric in LDS
-// first.
+// (and column by column for a mirror or a transposed copy) in 16-byte
+// non-temporal pieces; a diagonal tile of a symmetric product is made
+// exactly symmetric in LDS first.
 //
 // fp32 kernel (the fp32 NS mode): 64 x 64 x 16 tiles, four waves of 32 x 32,
 // v_mfma_f32_32x32x2f32, register-staged k-major LDS.
@@ -157,12 +159,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 #define GLOBAL_AS __attribute__((address_space(1)))
 
 // Global-address-space accesses (flat ones would also count against the LDS
-// counter that the LDS-only barrier waits on).
+// counter that the LDS-only barrier waits on), non-temporal: results and
+// parameters pass through once, and kept in L2 they would push out the
+// operand rows that neighbouring tiles are still reading.
 __device__ __forceinline__ u32x4_t gload_u32x4(const void* p) {
-  return *reinterpret_cast<const GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p));
+  return __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p)));
 }
 __device__ __forceinline__ void gstore_u32x4(void* p, u32x4_t v) {
-  *reinterpret_cast<GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p)) = v;
+  __builtin_nontemporal_store(v, reinterpret_cast<GLOBAL_AS u32x4_t*>(reinterpret_cast<uintptr_t>(p)));
 }
 __device__ __forceinline__ float gload_f32(const float* p) {
   return *reinterpret_cast<const GLOBAL_AS float*>(reinterpret_cast<uintptr_t>(p));
@@ -180,6 +184,25 @@ __device__ __forceinline__ void lds_barrier() {
 // sits in slot c ^ ((r >> 1) & 7).  A fragment read (16 lanes of a 128-bit
 // read per cycle: 16 consecutive rows, one chunk) then covers all 64 banks.
 __device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Buffer load into LDS (the LLVM intrinsic: descriptor, LDS address, bytes
+// per lane, per-lane offset, wave offset, immediate offset, cache bits).
+// Lane l writes bytes 16l..16l+15 of a 1 KB block at the LDS address; a lane
+// whose offset is outside the descriptor's range reads zeros.
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* lds, int size, int voffset, int soffset,
+                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// raw buffer descriptor (gfx9 layout): 48-bit base address, no stride,
+// `bytes` in range, default format word
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
 
 template <int BT, int kStages>
 __global__ void __launch_bounds__(256)
@@ -222,7 +245,15 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // DMA sources: load q of this wave fills LDS block idx = wave + 4q of the
   // stage (blocks 0 .. LOADS_PER_OP-1: A rows, the rest: B rows); lane l
   // writes slot l%8 of row 8*block + l/8, which holds chunk slot^swizzle.
-  const uint16_t* src[LOADS];
+  // Each operand is read through a buffer descriptor based at the tile's
+  // first row and the stage's first k (scalar registers, advanced per
+  // stage) with a fixed 32-bit byte offset per lane and load, so issuing a
+  // load costs no vector arithmetic; the range covers the BT rows of one
+  // stage (dimensions up to 2^22 keep it below 2^31 bytes).
+  const char* const a_base = static_cast<const char*>(T.A) + int64_t(tm) * BT * T.lda * 2;
+  const char* const b_base = static_cast<const char*>(T.B) + int64_t(tn) * BT * T.ldb * 2;
+  const int a_span = int((BT - 1) * T.lda * 2 + kRowBytes), b_span = int((BT - 1) * T.ldb * 2 + kRowBytes);
+  uint32_t voff[LOADS];
   int dst_off[LOADS];
 #pragma unroll
   for (int q = 0; q < LOADS; ++q) {
@@ -231,9 +262,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     const int blk = is_b ? idx - LOADS_PER_OP : idx;
     const int row = blk * kRowsPerLoad + (lane >> 3);
     const int chunk = slot_of(row, lane & 7);
-    const uint16_t* base = is_b ? static_cast<const uint16_t*>(T.B) + (int64_t(tn) * BT + row) * T.ldb
-                                : static_cast<const uint16_t*>(T.A) + (int64_t(tm) * BT + row) * T.lda;
-    src[q] = base + chunk * 8;
+    voff[q] = uint32_t(row * int(is_b ? T.ldb : T.lda) + chunk * 8) * 2u;
     dst_off[q] = (is_b ? OPB : 0) + blk * 1024;
   }
 
@@ -256,14 +285,6 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // stage `data` of the operands into ring slot `slot % kStages`
-  auto issue_stage = [&](int data, int slot) {
-    char* st = smem + (slot % kStages) * STB;
-#pragma unroll
-    for (int q = 0; q < LOADS; ++q)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
-                                       (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
-  };
   auto read_frags = [&](int s, int kq, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F], auto same) {
     constexpr int BOFF = decltype(same)::value ? 0 : OPB;
     const char* st = smem + (s % kStages) * STB + frag_off[kq];
@@ -322,12 +343,15 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // loads of a stage issued in quarter 3 (the rest go in the next quarter 0)
   constexpr int LQ3 = BT == 256 ? kLoadsEarly256 : LOADS / 2;
   constexpr int LQ0 = LOADS - LQ3;
+  // part h of stage `data`'s loads into ring slot `slot % kStages`
   auto issue_part = [&](int data, int slot, int h) {
     char* st = smem + (slot % kStages) * STB;
+    const i32x4_t ra = make_rsrc(a_base + data * kRowBytes, a_span);
+    const i32x4_t rb = make_rsrc(b_base + data * kRowBytes, b_span);
 #pragma unroll
     for (int q = h ? LQ3 : 0; q < (h ? LOADS : LQ3); ++q)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src[q] + data * kStageK),
-                                       (LDS_AS void*)(st + dst_off[q]), 16, 0, 0);
+      raw_buffer_load_lds(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(st + dst_off[q]), 16,
+                          int(voff[q]), 0, 0, 0);
   };
   // MFMAs of one quarter with the next quarter's reads and part of a stage's
   // loads interleaved; the reads come first in program order (the compiler
@@ -504,8 +528,9 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
 
   // scale, add, round and stage: fragment (i, j), register group g covers
   // row wm*WT + 32i + (lane & 31), columns wn*WT + 32j + 8g + 4(lane >> 5) + 0..3
-  {
-    const bool has_y = Y != nullptr;
+  // (one instance with Y and one without, so no group carries a branch)
+  auto stage_tile = [&](auto hy) {
+    constexpr bool has_y = decltype(hy)::value;
     const bool add_gamma = tm == tn && gamma != 0.f && wm == wn;
 #pragma unroll
     for (int i = 0; i < F; ++i) {
@@ -516,7 +541,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
 #pragma unroll
       for (int j = 0; j < F; ++j) {
         uint2 y[4];
-        if (has_y) {
+        if constexpr (has_y) {
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             y[g] = *reinterpret_cast<const uint2*>(srow + ((((wn * WT + j * 32) / 8 + g) ^ sw) << 4));
@@ -526,7 +551,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = alpha * acc[i][j][4 * g + r];
-          if (has_y) {
+          if constexpr (has_y) {
             v[0] = fmaf(beta, __uint_as_float(y[g].x << 16), v[0]);
             v[1] = fmaf(beta, __uint_as_float(y[g].x & 0xffff0000u), v[1]);
             v[2] = fmaf(beta, __uint_as_float(y[g].y << 16), v[2]);
@@ -543,7 +568,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
         __builtin_amdgcn_sched_barrier(0);       // bounds the live accumulator copies
       }
     }
-  }
+  };
+  if (Y)
+    stage_tile(std::true_type{});
+  else
+    stage_tile(std::false_type{});
   lds_barrier();
 
   // 8 x 4 block transposes: lane tq takes rows 8rb..8rb+7 of columns

@@ -98,10 +98,10 @@ struct TileRef {
 };
 
 // Number of XCDs that workgroups are dealt to round-robin, and the shape of
-// the groups of tiles walked together inside a task (one group is about as
-// many tiles as one XCD runs at once).
+// the groups of tiles walked together inside a task (one group is as many
+// 256-tiles as one XCD runs at once: 8 row panels by 4 column panels).
 constexpr int kNumXcd = 8;
-constexpr int kTileGroupRows = 4, kTileGroupCols = 4;
+constexpr int kTileGroupRows = 8, kTileGroupCols = 4;
 
 // One sum of the partial Gram matrices of a sharded matrix (the stand-in
 // for their all-reduce across tensor-parallel ranks): dst = sum over
