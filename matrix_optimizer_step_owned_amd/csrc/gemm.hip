@@ -825,6 +825,108 @@ gemm_f32_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__ 
                           T.diag_limit, mode);
 }
 
+// 128 x 128 x 32 tiles for batches with enough work to fill the chip: four
+// waves of 64 x 64 (2 x 2 fragments of 32 x 32), half the operand bytes per
+// flop of the 64 tile, and 64 MFMAs per wave per stage to cover the loads of
+// the next stage.  Operands are staged through registers into k-major LDS
+// rows (pitch BT + 2 words: the four k rows a wave writes at once start 8
+// banks apart).
+constexpr int kF32BigTile = kTileF32Big;
+constexpr int kF32BigBK = 32;
+constexpr int kF32BigPitch = kF32BigTile + 2;
+
+__global__ void __launch_bounds__(256)
+gemm_f32_big_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__ map) {
+  constexpr int BT = kF32BigTile, BK = kF32BigBK, LDP = kF32BigPitch;
+  constexpr int NLD = BT * BK / 4 / 256;          // float4 loads per thread per operand per stage
+  __shared__ __attribute__((aligned(16))) float As[2][BK][LDP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDP];
+
+  const TileRef ref = map[blockIdx.x];
+  const int tm = ref.tm, tn = ref.tn;
+  const GemmTask& T = tasks[ref.task];
+  const int64_t lda = T.lda, ldb = T.ldb;
+  const float* __restrict__ A = static_cast<const float*>(T.A) + int64_t(tm) * BT * lda;
+  const float* __restrict__ B = static_cast<const float*>(T.B) + int64_t(tn) * BT * ldb;
+  const int nk = T.K / BK;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // thread t stages rows (t >> 3) + 32i, k = 4*(t & 7) .. +3 of both operands
+  const int lrow = t >> 3, lk = (t & 7) * 4;
+
+  float4 ra[NLD], rb[NLD];
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  for (int kt = 0; kt <= nk; ++kt) {
+    if (kt > 0) {
+      const int buf = (kt - 1) & 1;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int row = lrow + 32 * i;
+        As[buf][lk + 0][row] = ra[i].x; As[buf][lk + 1][row] = ra[i].y;
+        As[buf][lk + 2][row] = ra[i].z; As[buf][lk + 3][row] = ra[i].w;
+        Bs[buf][lk + 0][row] = rb[i].x; Bs[buf][lk + 1][row] = rb[i].y;
+        Bs[buf][lk + 2][row] = rb[i].z; Bs[buf][lk + 3][row] = rb[i].w;
+      }
+      __syncthreads();
+    }
+    if (kt < nk) {
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        ra[i] = gload16f(A + int64_t(lrow + 32 * i) * lda + k0 + lk);
+        rb[i] = gload16f(B + int64_t(lrow + 32 * i) * ldb + k0 + lk);
+      }
+    }
+    if (kt > 0) {
+      const int cur = (kt - 1) & 1;
+#pragma unroll
+      for (int kk = 0; kk < BK / 2; ++kk) {
+        const int k = kk * 2 + (lane >> 5);
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = As[cur][k][wm * 64 + i * 32 + (lane & 31)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = Bs[cur][k][wn * 64 + j * 32 + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  const float s = T.scale ? *T.scale : 1.f;
+  const float alpha = T.alpha * spow(s, T.alpha_pow);
+  const float beta = T.beta * spow(s, T.beta_pow);
+  float* __restrict__ C = static_cast<float*>(T.C);
+  float* __restrict__ Ct = static_cast<float*>(T.Ct);
+  const float* __restrict__ Y = static_cast<const float*>(T.Y);
+  const int mode = T.sym ? (tm != tn ? 1 : 2) : (Ct ? 3 : 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row0 = tm * BT + wm * 64 + i * 32 + (lane >> 5) * 4;
+      const int col = tn * BT + wn * 64 + j * 32 + (lane & 31);
+      if (Y)
+        store_fragment<true>(acc[i][j], C, T.ldc, Ct, T.ldct, Y, T.ldy, row0, col, alpha, beta, T.gamma,
+                             T.diag_limit, mode);
+      else
+        store_fragment<false>(acc[i][j], C, T.ldc, Ct, T.ldct, Y, T.ldy, row0, col, alpha, beta, T.gamma,
+                              T.diag_limit, mode);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmTask* tasks_dev, const TileRef* map_dev, int64_t ntiles,
@@ -846,9 +948,15 @@ hipError_t launch_gemm_bf16(const GemmTask* tasks_dev, const TileRef* map_dev, i
 hipError_t launch_gemm_f32(const GemmTask* tasks_dev, const TileRef* map_dev, int64_t ntiles,
                            int tile, hipStream_t stream) {
   if (ntiles <= 0) return hipSuccess;
-  if (tile != kF32Tile) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, stream,
-                     tasks_dev, map_dev);
+  if (tile == kF32Tile) {
+    hipLaunchKernelGGL(gemm_f32_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, stream,
+                       tasks_dev, map_dev);
+  } else if (tile == kF32BigTile) {
+    hipLaunchKernelGGL(gemm_f32_big_kernel, dim3(static_cast<unsigned>(ntiles)), dim3(256), 0, stream,
+                       tasks_dev, map_dev);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -211,6 +211,10 @@ hipError_t launch_clip_scale(const ClipItem* items_dev, int n, int64_t nblocks, 
 constexpr int kTileBf16 = 128;
 constexpr int kTileBf16Big = 256;
 constexpr int kTileF32 = 64;
+constexpr int kTileF32Big = 128;
+// fp32 products use 128-tiles when the first NS stage has at least this many
+// of them (two per CU, two waves of blocks), else 64-tiles.
+constexpr int64_t kF32BigTileMinCount = 1024;
 // 256-tiles are used when the first NS stage has at least this many of them
 // and at least half of them belong to matrices kBigTileMinDim or more wide.
 constexpr int64_t kBigTileMinCount = 128;

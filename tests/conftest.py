@@ -30,12 +30,15 @@ def lib():
     return dm
 
 
-@pytest.fixture(params=["auto", "256"])
+@pytest.fixture(params=["auto", "big"])
 def gemm_tile(request, monkeypatch):
-    """Run a GPU test with the library's own tile choice and with the
-    256 x 256 bf16 tiles forced (DMUON_GEMM_TILE)."""
+    """Run a GPU test with the library's own tile choice and with the large
+    tiles forced: 256 x 256 for bf16 products (DMUON_GEMM_TILE), 128 x 128
+    for fp32 ones (DMUON_GEMM_TILE_F32)."""
     if request.param == "auto":
         monkeypatch.delenv("DMUON_GEMM_TILE", raising=False)
+        monkeypatch.delenv("DMUON_GEMM_TILE_F32", raising=False)
     else:
-        monkeypatch.setenv("DMUON_GEMM_TILE", request.param)
+        monkeypatch.setenv("DMUON_GEMM_TILE", "256")
+        monkeypatch.setenv("DMUON_GEMM_TILE_F32", "128")
     return request.param

@@ -192,6 +192,29 @@ def test_plan_tile_choice(dm):
     assert mixed["matrices"][-1]["tile"] == 128 and mixed["matrices"][-1]["m_pad"] == 128
     assert {l["tile"] for l in mixed["launches"]} == {128, 256}
     assert dm.dmuon_plan_describe([(4096, 4096)], ns_precision="f32")["tile"] == 64
+    # fp32 products: 128-tiles once the first stage has two waves of them;
+    # matrices narrower than 128 keep 64-tiles in launches of their own
+    w4 = [(m.rows, m.cols) for m in di.workload(4).matrices]
+    p4 = dm.dmuon_plan_describe(w4, ns_precision="f32")
+    assert p4["tile"] == 128 and all(m["tile"] == 128 for m in p4["matrices"])
+    assert all(m["m_pad"] % 128 == 0 and m["n_pad"] % 128 == 0 for m in p4["matrices"])
+    p4m = dm.dmuon_plan_describe(w4 + [(64, 300)], ns_precision="f32")
+    assert p4m["matrices"][-1]["tile"] == 64 and {l["tile"] for l in p4m["launches"]} == {64, 128}
+
+
+def test_plan_tile_override(dm, monkeypatch):
+    """DMUON_GEMM_TILE / DMUON_GEMM_TILE_F32 force the tile edge of their
+    precision only."""
+    monkeypatch.setenv("DMUON_GEMM_TILE", "256")
+    monkeypatch.setenv("DMUON_GEMM_TILE_F32", "128")
+    assert dm.dmuon_plan_describe([(300, 500)])["tile"] == 256
+    p = dm.dmuon_plan_describe([(300, 500), (100, 700)], ns_precision="f32")
+    assert p["tile"] == 128 and [m["tile"] for m in p["matrices"]] == [128, 64]
+    monkeypatch.setenv("DMUON_GEMM_TILE_F32", "64")
+    assert dm.dmuon_plan_describe([(m.rows, m.cols) for m in __import__("dmuon_inputs").workload(4).matrices],
+                                  ns_precision="f32")["tile"] == 64
+    monkeypatch.delenv("DMUON_GEMM_TILE")
+    assert dm.dmuon_plan_describe([(300, 500)])["tile"] == 128
 
 
 def test_tile_maps_cover_every_tile_once(dm):

@@ -56,8 +56,6 @@ def _check(got_parts, ref_parts, split, tol, what):
 @pytest.mark.parametrize("backend", ["gram", "direct"])
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 def test_sharded_parity(lib, gemm_tile, backend, prec):
-    if gemm_tile == "256" and prec == "f32":
-        pytest.skip("the tile override applies to bf16 products")
     io = "f32" if prec == "f32" else "bf16"
     ins, exact = _inputs(CASES, io, seed=1)
     outs = [[torch.full_like(t, float("nan")) for t in mat] for mat in ins]
