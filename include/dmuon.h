@@ -31,8 +31,10 @@
  *   - Threads: entry points may be called from several host threads; calls
  *     enqueued on different streams must use different workspaces.
  *   - Environment: DMUON_GEMM_TILE=128 or 256 forces the tile edge of the
- *     bf16 NS products (default: 256 for large batches, 128 otherwise); it
- *     changes the workspace size and the summation order, not the method.
+ *     bf16 NS products (default: 256 for large batches, 128 otherwise), and
+ *     DMUON_GEMM_TILE_F32=64 or 128 that of the fp32 ones (default: 128 for
+ *     large batches, 64 otherwise); each changes the workspace size and the
+ *     summation order, not the method.
  */
 #ifndef DMUON_H
 #define DMUON_H
