@@ -38,8 +38,9 @@
 // non-temporal pieces; a diagonal tile of a symmetric product is made
 // exactly symmetric in LDS first.
 //
-// fp32 kernel (the fp32 NS mode): 64 x 64 x 16 tiles, four waves of 32 x 32,
-// v_mfma_f32_32x32x2f32, register-staged k-major LDS.
+// fp32 kernels (the fp32 NS mode): v_mfma_f32_32x32x2f32, register-staged
+// k-major LDS, per-fragment epilogue; 64 x 64 x 16 tiles (four waves of
+// 32 x 32) or 128 x 128 x 32 tiles (four waves of 64 x 64).
 #include <cstdlib>
 #include <type_traits>
 
