@@ -40,7 +40,7 @@
 //
 // fp32 kernels (the fp32 NS mode): v_mfma_f32_32x32x2f32, register-staged
 // k-major LDS, per-fragment epilogue; 64 x 64 x 16 tiles (four waves of
-// 32 x 32) or 128 x 128 x 32 tiles (four waves of 64 x 64).
+// 32 x 32) or 128 x 128 x 16 tiles (four waves of 64 x 64).
 #include <cstdlib>
 #include <type_traits>
 
@@ -826,20 +826,25 @@ gemm_f32_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__ 
                           T.diag_limit, mode);
 }
 
-// 128 x 128 x 32 tiles for batches with enough work to fill the chip: four
+// 128 x 128 x 16 tiles for batches with enough work to fill the chip: four
 // waves of 64 x 64 (2 x 2 fragments of 32 x 32), half the operand bytes per
-// flop of the 64 tile, and 64 MFMAs per wave per stage to cover the loads of
-// the next stage.  Operands are staged through registers into k-major LDS
-// rows (pitch BT + 2 words: the four k rows a wave writes at once start 8
-// banks apart).
+// flop of the 64 tile, 32 MFMAs per wave per stage to cover the loads of the
+// next stage, two blocks per CU.  Operands are staged through registers into
+// k-major LDS rows of pitch BT + 2 words.  (Measured on 4096 plain tiles,
+// K = 4096: 16-k stages 132 TFLOP/s, 32-k 127, 64-k 102; pitches BT + 2,
+// BT + 4 and BT + 32 within 3 %.)
 constexpr int kF32BigTile = kTileF32Big;
-constexpr int kF32BigBK = 32;
+constexpr int kF32BigBK = 16;
 constexpr int kF32BigPitch = kF32BigTile + 2;
 
 __global__ void __launch_bounds__(256)
 gemm_f32_big_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__ map) {
   constexpr int BT = kF32BigTile, BK = kF32BigBK, LDP = kF32BigPitch;
-  constexpr int NLD = BT * BK / 4 / 256;          // float4 loads per thread per operand per stage
+  constexpr int KCH = BK / 4;                      // float4 chunks per operand row of a stage
+  constexpr int RPP = 256 / KCH;                   // operand rows covered by one pass of the block
+  constexpr int NLD = BT / RPP;                    // float4 loads per thread per operand per stage
+  static_assert(BK % 4 == 0 && 256 % KCH == 0 && BT % RPP == 0 && NLD * RPP * KCH * 4 == BT * BK,
+                "the block's loads cover the BT x BK operand slab exactly once");
   __shared__ __attribute__((aligned(16))) float As[2][BK][LDP];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK][LDP];
 
@@ -855,8 +860,8 @@ gemm_f32_big_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restric
   const int lane = t & 63;
   const int wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  // thread t stages rows (t >> 3) + 32i, k = 4*(t & 7) .. +3 of both operands
-  const int lrow = t >> 3, lk = (t & 7) * 4;
+  // thread t stages rows t / KCH + RPP*i, k = 4*(t % KCH) .. +3 of both operands
+  const int lrow = t / KCH, lk = (t % KCH) * 4;
 
   float4 ra[NLD], rb[NLD];
   f32x16_t acc[2][2];
@@ -872,7 +877,7 @@ gemm_f32_big_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restric
       const int buf = (kt - 1) & 1;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int row = lrow + 32 * i;
+        const int row = lrow + RPP * i;
         As[buf][lk + 0][row] = ra[i].x; As[buf][lk + 1][row] = ra[i].y;
         As[buf][lk + 2][row] = ra[i].z; As[buf][lk + 3][row] = ra[i].w;
         Bs[buf][lk + 0][row] = rb[i].x; Bs[buf][lk + 1][row] = rb[i].y;
@@ -884,8 +889,8 @@ gemm_f32_big_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restric
       const int k0 = kt * BK;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        ra[i] = gload16f(A + int64_t(lrow + 32 * i) * lda + k0 + lk);
-        rb[i] = gload16f(B + int64_t(lrow + 32 * i) * ldb + k0 + lk);
+        ra[i] = gload16f(A + int64_t(lrow + RPP * i) * lda + k0 + lk);
+        rb[i] = gload16f(B + int64_t(lrow + RPP * i) * ldb + k0 + lk);
       }
     }
     if (kt > 0) {
