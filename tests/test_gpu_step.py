@@ -141,9 +141,11 @@ def test_step_nan_isolation_and_skip(lib):
     assert torch.equal(p3[2], p2[2])
 
 
-def test_step_deterministic_and_resume(lib):
+@pytest.mark.parametrize("prec", ["bf16", "f32"])
+def test_step_deterministic_and_resume(lib, prec, gemm_tile):
     """Two runs are bit-identical, and a run stopped after step 2 and resumed
-    from copies of (params, momenta) matches the uninterrupted run."""
+    from copies of (params, momenta) matches the uninterrupted run (every
+    GEMM kernel: both precisions, both tile edges of each)."""
     w = di.workload(0)
     shapes = [(256, 512), (640, 256), (1024, 1024)]
     def init():
@@ -155,18 +157,18 @@ def test_step_deterministic_and_resume(lib):
     pa, ma = init()
     pb, mb = init()
     for s in range(4):
-        lib.dmuon_step(pa, grads[s], ma)
-        lib.dmuon_step(pb, grads[s], mb)
+        lib.dmuon_step(pa, grads[s], ma, ns_precision=prec)
+        lib.dmuon_step(pb, grads[s], mb, ns_precision=prec)
     pc, mc = init()
     for s in range(2):
-        lib.dmuon_step(pc, grads[s], mc)
+        lib.dmuon_step(pc, grads[s], mc, ns_precision=prec)
     torch.cuda.synchronize()
     saved_p = [p.cpu().clone() for p in pc]
     saved_m = [m.cpu().clone() for m in mc]
     pd = [p.to(DEV) for p in saved_p]
     md = [m.to(DEV) for m in saved_m]
     for s in range(2, 4):
-        lib.dmuon_step(pd, grads[s], md)
+        lib.dmuon_step(pd, grads[s], md, ns_precision=prec)
     torch.cuda.synchronize()
     for i in range(len(shapes)):
         assert torch.equal(pa[i], pb[i]) and torch.equal(ma[i], mb[i])
