@@ -237,17 +237,32 @@ def _matrices(params, grads, momenta) -> ctypes.Array:
     return arr
 
 
-def _stream(stream, device) -> int:
+def _torch_stream(stream, device):
+    """The stream the library's kernels go to, as a torch stream: the
+    current stream by default, a torch stream as given, or a raw HIP stream
+    handle wrapped as an external stream."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
-def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+def _stream(stream, device) -> int:
+    return _torch_stream(stream, device).cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor], stream=None):
+    """The caller's workspace, or one allocated here.  An allocated one
+    belongs to the stream the kernels run on (so PyTorch's caching allocator
+    hands its bytes to nothing else until that stream has passed the
+    kernels that use them), whichever stream is current."""
     if nbytes == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ts = _torch_stream(stream, device)
+        with torch.cuda.stream(ts):
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return workspace, workspace.numel() * workspace.element_size()
@@ -281,7 +296,7 @@ def dmuon_step(params: List[torch.Tensor], grads: List[Optional[torch.Tensor]],
     mats = _matrices(params, grads, momenta)
     h, _keep = _hparams(**hp)
     nbytes = int(_lib.dmuon_step_workspace_size(mats, n, ctypes.byref(h)))
-    ws, wsb = _workspace(nbytes, params[0].device, workspace)
+    ws, wsb = _workspace(nbytes, params[0].device, workspace, stream)
     wsp = ws.data_ptr() if ws is not None else None
     st = _stream(stream, params[0].device)
     if grad_scale is None:
@@ -321,7 +336,7 @@ def dmuon_momentum(grads: List[torch.Tensor], momenta: List[torch.Tensor],
         raise ValueError("sumsq must be a float64 tensor of n entries")
     h, _keep = _hparams(momentum=momentum, nesterov=nesterov)
     nbytes = int(_lib.dmuon_momentum_workspace_size(mats, n))
-    ws, wsb = _workspace(nbytes, grads[0].device, workspace)
+    ws, wsb = _workspace(nbytes, grads[0].device, workspace, stream)
     _check(_lib.dmuon_momentum(mats, n, ctypes.byref(h), _ptrs(ns_inputs), dt, sumsq.data_ptr(),
                                ws.data_ptr() if ws is not None else None, wsb,
                                _stream(stream, grads[0].device)), "dmuon_momentum")
@@ -351,7 +366,7 @@ def dmuon_orthogonalize(inputs: List[torch.Tensor], outputs: List[torch.Tensor],
     cols = (ctypes.c_int64 * n)(*[int(t.shape[1]) for t in inputs])
     h, _keep = _hparams(**hp)
     nbytes = int(_lib.dmuon_orthogonalize_workspace_size(rows, cols, n, ctypes.byref(h)))
-    ws, wsb = _workspace(nbytes, inputs[0].device, workspace)
+    ws, wsb = _workspace(nbytes, inputs[0].device, workspace, stream)
     _check(_lib.dmuon_orthogonalize(_ptrs(inputs), _ptrs(outputs), rows, cols, n, dt, ctypes.byref(h),
                                     ws.data_ptr() if ws is not None else None, wsb,
                                     _stream(stream, inputs[0].device)), "dmuon_orthogonalize")
@@ -414,7 +429,7 @@ def dmuon_orthogonalize_sharded(inputs: List[List[torch.Tensor]], outputs: List[
     h, _keep2 = _hparams(**hp)
     nbytes = int(_lib.dmuon_orthogonalize_sharded_workspace_size(arr, n, ctypes.byref(h)))
     dev = inputs[0][0].device
-    ws, wsb = _workspace(nbytes, dev, workspace)
+    ws, wsb = _workspace(nbytes, dev, workspace, stream)
     _check(_lib.dmuon_orthogonalize_sharded(arr, n, dt, ctypes.byref(h),
                                             ws.data_ptr() if ws is not None else None, wsb,
                                             _stream(stream, dev)), "dmuon_orthogonalize_sharded")
@@ -466,7 +481,7 @@ def dmuon_adamw_step(params: List[torch.Tensor], grads: List[Optional[torch.Tens
         ta[i].group = int(group_index[i])
         if gr is not None and not gr.is_contiguous():
             raise ValueError(f"grads[{i}] must be contiguous")
-    ws, wsb = _workspace(dmuon_adamw_workspace_size(n), params[0].device, workspace)
+    ws, wsb = _workspace(dmuon_adamw_workspace_size(n), params[0].device, workspace, stream)
     _check(_lib.dmuon_adamw_step(ta, n, ga, len(groups), ws.data_ptr() if ws is not None else None, wsb,
                                  _stream(stream, params[0].device)), "dmuon_adamw_step")
 
@@ -510,7 +525,7 @@ def dmuon_apply_update(params: List[torch.Tensor], updates: List[torch.Tensor], 
             raise ValueError(f"updates[{i}] must have the param's shape and one dtype")
     h, _keep = _hparams(lr=lr, weight_decay=weight_decay)
     nbytes = int(_lib.dmuon_apply_update_workspace_size(n))
-    ws, wsb = _workspace(nbytes, params[0].device, workspace)
+    ws, wsb = _workspace(nbytes, params[0].device, workspace, stream)
     _check(_lib.dmuon_apply_update(mats, n, _ptrs(updates), dt, ctypes.byref(h),
                                    ws.data_ptr() if ws is not None else None, wsb,
                                    _stream(stream, params[0].device)), "dmuon_apply_update")
@@ -545,10 +560,11 @@ def dmuon_clip_grad_norm(grads: List[torch.Tensor], max_norm, *, norm_type: floa
         return torch.zeros(nb, dtype=torch.float64)
     device = grads[0].device
     if total_norm is None:
-        total_norm = torch.empty(nb, dtype=torch.float64, device=device)
+        with torch.cuda.stream(_torch_stream(stream, device)):
+            total_norm = torch.empty(nb, dtype=torch.float64, device=device)
     mx = (ctypes.c_double * nb)(*[float(v) for v in max_norm])
     nbytes = int(_lib.dmuon_clip_workspace_size(arr, n, nb)) if n else 0
-    ws, wsb = _workspace(nbytes, device, workspace)
+    ws, wsb = _workspace(nbytes, device, workspace, stream)
     _check(_lib.dmuon_clip_grad_norm(arr, n, nb, mx, float(norm_type), total_norm.data_ptr(),
                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream, device)),
            "dmuon_clip_grad_norm")
@@ -576,13 +592,14 @@ def dmuon_clip_coefficients(grads: List[torch.Tensor], max_norm, *, norm_type: f
             raise ValueError(f"grads[{i}] must be contiguous")
         arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = g.numel(), g.data_ptr(), _dtype(g), int(buckets[i])
     device = grads[0].device if n else torch.device("cpu")
-    if coefs is None:
-        coefs = torch.ones(nb, dtype=torch.float64, device=device)
     if n == 0:
-        return coefs
+        return coefs if coefs is not None else torch.ones(nb, dtype=torch.float64, device=device)
+    if coefs is None:
+        with torch.cuda.stream(_torch_stream(stream, device)):
+            coefs = torch.ones(nb, dtype=torch.float64, device=device)
     mx = (ctypes.c_double * nb)(*[float(v) for v in max_norm])
     nbytes = int(_lib.dmuon_clip_workspace_size(arr, n, nb))
-    ws, wsb = _workspace(nbytes, device, workspace)
+    ws, wsb = _workspace(nbytes, device, workspace, stream)
     _check(_lib.dmuon_clip_coefficients(arr, n, nb, mx, float(norm_type),
                                         total_norm.data_ptr() if total_norm is not None else None,
                                         coefs.data_ptr(), ws.data_ptr() if ws is not None else None, wsb,

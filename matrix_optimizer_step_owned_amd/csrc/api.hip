@@ -169,6 +169,7 @@ struct Launch {
 };
 
 struct Plan {
+  std::string key;   // the plan cache key: shapes, groups, precision, backend, coefficients
   int n = 0;
   int32_t prec = 0;
   int ns_steps = 0;
@@ -633,6 +634,7 @@ std::shared_ptr<Plan> get_plan(const std::vector<ShapeSpec>& shapes, const std::
   }
   auto P = build_plan(shapes, groups, prec, backend, cf, with_ns, tile_override);
   layout_plan(*P, cf, with_ns);
+  P->key = key;
   std::lock_guard<std::mutex> lk(g_plan_mu);
   if (g_plans.size() > 256) g_plans.clear();
   g_plans.emplace(key, P);
@@ -656,18 +658,33 @@ std::shared_ptr<Plan> get_plan(const std::vector<int64_t>& rows, const std::vect
 // device check and launch-table staging
 // ---------------------------------------------------------------------------
 
+// Launch tables reach the device as one copy per call from a pinned host
+// image.  An image depends only on what it was filled from (the plan and
+// the caller's pointers and scalars, its `key`), so images are cached per
+// device and never changed while cached: a call whose key matches an image
+// enqueues the copy and nothing else, and any number of copies of one image
+// may be in flight.  Every copy records an event; an image is refilled for
+// another key only once all its events have completed, which the host
+// queries without waiting.  The host blocks only when more than
+// kMaxTableImages images on one device all still have copies in flight.
+constexpr size_t kTableImagesKept = 16;
+constexpr size_t kMaxTableImages = 64;
+
+struct TableImage {
+  std::string key;
+  void* host = nullptr;   // pinned; `bytes` valid, `cap` allocated
+  size_t cap = 0, bytes = 0;
+  std::vector<hipEvent_t> pending;   // events behind copies not yet known complete
+  uint64_t last_use = 0;
+};
+
 struct DeviceState {
   bool checked = false;
   bool ok = false;
   std::string arch;
-  struct Slot {
-    void* host = nullptr;
-    size_t cap = 0;
-    hipEvent_t ev = nullptr;
-    bool pending = false;
-  };
-  Slot slots[4];
-  int next = 0;
+  std::vector<std::unique_ptr<TableImage>> images;
+  std::vector<hipEvent_t> free_events;
+  uint64_t clock = 0;
 };
 
 std::mutex g_dev_mu;
@@ -689,35 +706,124 @@ int current_device_state(DeviceState** out) {
   return DMUON_OK;
 }
 
-// Copy `bytes` of launch table, built by `fill` into pinned host memory, to
-// device address `dst` on `stream`.  A ring of four pinned buffers, each
-// guarded by an event, lets the host run ahead of the device.
+// Drops the image's completed events (returned to the pool); true when none
+// is left in flight.
+int retire_events(DeviceState& d, TableImage& im, bool* idle) {
+  size_t k = 0;
+  for (hipEvent_t e : im.pending) {
+    const hipError_t q = hipEventQuery(e);
+    if (q == hipSuccess) {
+      d.free_events.push_back(e);
+    } else if (q == hipErrorNotReady) {
+      im.pending[k++] = e;
+    } else {
+      return fail(DMUON_ERR_HIP, std::string("hipEventQuery: ") + hipGetErrorString(q));
+    }
+  }
+  im.pending.resize(k);
+  *idle = k == 0;
+  return DMUON_OK;
+}
+
+// Appends the object representation of trivially copyable values to a key.
+struct KeyBuf {
+  std::string s;
+  template <class T>
+  KeyBuf& put(const T& v) {
+    s.append(reinterpret_cast<const char*>(&v), sizeof(T));
+    return *this;
+  }
+  KeyBuf& put_str(const std::string& v) {
+    put(v.size());
+    s.append(v);
+    return *this;
+  }
+};
+
+// Copy `bytes` of launch table to device address `dst` on `stream`.  `key`
+// must hold everything `fill` reads; `fill` writes the table into a zeroed
+// host buffer and runs only when no cached image matches.
 template <class Fill>
-int stage_table(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
+int stage_table(void* dst, size_t bytes, hipStream_t stream, const std::string& key, Fill fill) {
   std::lock_guard<std::mutex> lk(g_dev_mu);
   DeviceState* d = nullptr;
   int st = current_device_state(&d);
   if (st != DMUON_OK) return st;
-  DeviceState::Slot& s = d->slots[d->next];
-  d->next = (d->next + 1) % 4;
-  if (s.pending) {
-    DMUON_HIP_TRY(hipEventSynchronize(s.ev));
-    s.pending = false;
+  KeyBuf full;
+  full.put(dst).put(bytes).put_str(key);
+  TableImage* im = nullptr;
+  for (auto& p : d->images)
+    if (p->bytes == bytes && p->key == full.s) { im = p.get(); break; }
+  if (!im) {
+    // an idle image to refill (least recently used first), else a new one
+    std::vector<TableImage*> by_age;
+    for (auto& p : d->images) by_age.push_back(p.get());
+    std::sort(by_age.begin(), by_age.end(), [](const TableImage* a, const TableImage* b) {
+      return a->last_use < b->last_use;
+    });
+    if (d->images.size() >= kTableImagesKept) {
+      for (TableImage* c : by_age) {
+        bool idle = false;
+        st = retire_events(*d, *c, &idle);
+        if (st != DMUON_OK) return st;
+        if (idle) { im = c; break; }
+      }
+    }
+    if (!im && d->images.size() >= kMaxTableImages) {
+      // every image has a copy in flight: wait for the oldest
+      im = by_age.front();
+      for (hipEvent_t e : im->pending) {
+        DMUON_HIP_TRY(hipEventSynchronize(e));
+        d->free_events.push_back(e);
+      }
+      im->pending.clear();
+    }
+    if (!im) {
+      d->images.push_back(std::make_unique<TableImage>());
+      im = d->images.back().get();
+    }
+    if (im->cap < bytes) {
+      if (im->host) DMUON_HIP_TRY(hipHostFree(im->host));
+      im->host = nullptr;
+      im->cap = 0;
+      size_t cap = size_t(1) << 16;
+      while (cap < bytes) cap <<= 1;
+      DMUON_HIP_TRY(hipHostMalloc(&im->host, cap, hipHostMallocDefault));
+      im->cap = cap;
+    }
+    im->key.clear();   // not a valid image until filled
+    std::memset(im->host, 0, bytes);
+    fill(static_cast<char*>(im->host));
+    im->key = full.s;
+    im->bytes = bytes;
   }
-  if (s.cap < bytes) {
-    if (s.host) DMUON_HIP_TRY(hipHostFree(s.host));
-    s.host = nullptr;
-    s.cap = 0;
-    const size_t cap = std::max<size_t>(align_up(bytes, 1 << 16), 1 << 16);
-    DMUON_HIP_TRY(hipHostMalloc(&s.host, cap, hipHostMallocDefault));
-    s.cap = cap;
+  im->last_use = ++d->clock;
+  bool idle = false;
+  st = retire_events(*d, *im, &idle);
+  if (st != DMUON_OK) return st;
+  hipEvent_t ev = nullptr;
+  if (!d->free_events.empty()) {
+    ev = d->free_events.back();
+    d->free_events.pop_back();
+  } else {
+    DMUON_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
   }
-  if (!s.ev) DMUON_HIP_TRY(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
-  std::memset(s.host, 0, bytes);
-  fill(static_cast<char*>(s.host));
-  DMUON_HIP_TRY(hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream));
-  DMUON_HIP_TRY(hipEventRecord(s.ev, stream));
-  s.pending = true;
+  const hipError_t ce = hipMemcpyAsync(dst, im->host, bytes, hipMemcpyHostToDevice, stream);
+  if (ce != hipSuccess) {
+    d->free_events.push_back(ev);
+    return fail(DMUON_ERR_HIP, std::string("table copy: ") + hipGetErrorString(ce));
+  }
+  const hipError_t re = hipEventRecord(ev, stream);
+  if (re != hipSuccess) {
+    // the copy may be in flight with no event behind it: the buffer is left
+    // allocated and no image refers to it any more
+    im->host = nullptr;
+    im->cap = im->bytes = 0;
+    im->key.clear();
+    d->free_events.push_back(ev);
+    return fail(DMUON_ERR_HIP, std::string("table event: ") + hipGetErrorString(re));
+  }
+  im->pending.push_back(ev);
   return DMUON_OK;
 }
 
@@ -963,15 +1069,29 @@ const char* dmuon_status_string(int status) {
 const char* dmuon_last_error(void) { return g_last_error.c_str(); }
 
 const char* dmuon_backend_info(void) {
-  return "{\"arch\": \"gfx950\", "
-         "\"ns_gemm_bf16\": \"grouped 128x128x64 tiles, 4 waves of 64x64, "
-         "v_mfma_f32_32x32x16_bf16, fp32 accumulate, swizzled LDS double buffer; "
-         "NT symmetric (upper-triangle tiles, mirrored store) and NN (register-transposed B)\", "
-         "\"ns_gemm_f32\": \"grouped 64x64x16 tiles, v_mfma_f32_32x32x2f32\", "
-         "\"elementwise\": \"64x64 tiles, 256 threads, LDS transpose for tall matrices, "
-         "wave-shuffle sum of squares with fp64 per-matrix finish\", "
-         "\"gram_rule\": \"ns_backend gram uses the Gram form when max(m,n) >= 2*min(m,n), "
-         "the direct form otherwise\"}";
+  // built from the constants the planner and the launchers use
+  static const std::string info = [] {
+    std::ostringstream os;
+    os << "{\"arch\": \"gfx950\", "
+       << "\"ns_gemm_bf16\": {\"kernel\": \"gemm_bf16_kernel\", \"tiles\": [" << kTileBf16 << ", " << kTileBf16Big
+       << "], \"waves\": 4, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"accumulate\": \"f32\", "
+       << "\"stage_k\": 64, \"lds_stages\": 2, \"operand_loads\": \"buffer_load_dwordx4 to LDS\", "
+       << "\"big_tile_rule\": {\"min_first_stage_tiles\": " << kBigTileMinCount
+       << ", \"min_wide_share\": 0.5, \"wide_min_dim\": " << kBigTileMinDim
+       << ", \"min_matrix_dim\": " << kTileBf16Big << "}, "
+       << "\"products\": \"NT (K-contiguous operands); symmetric results as upper-triangle tiles "
+          "stored with their mirror\"}, "
+       << "\"ns_gemm_f32\": {\"kernel\": \"gemm_f32_kernel / gemm_f32_big_kernel\", \"tiles\": [" << kTileF32
+       << ", " << kTileF32Big << "], \"waves\": 4, \"mfma\": \"v_mfma_f32_32x32x2f32\", \"stage_k\": 16, "
+       << "\"big_tile_rule\": {\"min_first_stage_tiles\": " << kF32BigTileMinCount
+       << ", \"min_matrix_dim\": " << kTileF32Big << "}}, "
+       << "\"tile_override_env\": {\"bf16\": \"DMUON_GEMM_TILE\", \"f32\": \"DMUON_GEMM_TILE_F32\"}, "
+       << "\"elementwise\": {\"tile\": " << kEwTile << ", \"threads\": " << kEwThreads
+       << ", \"sum_of_squares\": \"wave shuffles, fp64 per-matrix finish\"}, "
+       << "\"gram_rule\": {\"gram_form_when_n_at_least_m_times\": 2}}";
+    return os.str();
+  }();
+  return info.c_str();
 }
 
 // ---- dmuon_step ------------------------------------------------------------
@@ -1054,7 +1174,13 @@ static int step_impl(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_
     const dmuon_matrix_t& m = mats[active[j]];
     fused[j] = {m.param, m.param_dtype, lr_eff_of(hp->lr, m.rows, m.cols), decay};
   }
-  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("step").put_str(P.key).put(hp->lr).put(hp->weight_decay);
+  for (int j = 0; j < P.n; ++j) {
+    key.put(mats[active[j]]);
+    key.put(grad_scale ? grad_scale[active[j]] : nullptr);
+  }
+  st = stage_table(ws, P.table_bytes, stream, key.s, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
     for (int j = 0; j < P.n; ++j) {
       const dmuon_matrix_t& m = mats[active[j]];
@@ -1185,7 +1311,10 @@ int dmuon_momentum(const dmuon_matrix_t* mats, int32_t n, const dmuon_hparams_t*
   if (st) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
-  st = stage_table(ws, P.off_ewmats + sizeof(EwMat) * P.n, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("momentum").put_str(P.key).put(ns_input_dtype);
+  for (int j = 0; j < P.n; ++j) key.put(mats[active[j]]).put(ns_input[active[j]]).put(active[j]);
+  st = stage_table(ws, P.off_ewmats + sizeof(EwMat) * P.n, stream, key.s, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
     for (int j = 0; j < P.n; ++j) {
       const dmuon_matrix_t& m = mats[active[j]];
@@ -1288,7 +1417,10 @@ int dmuon_orthogonalize(const void* const* in, void* const* out, const int64_t* 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
   const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
-  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("orthogonalize").put_str(P.key).put(io_dtype);
+  for (int j = 0; j < P.n; ++j) key.put(in[j]).put(out[j]);
+  st = stage_table(ws, P.table_bytes, stream, key.s, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
     for (int j = 0; j < P.n; ++j) {
       const MatLayout& L = P.mats[j];
@@ -1424,7 +1556,10 @@ int dmuon_orthogonalize_sharded(const dmuon_sharded_t* mats, int32_t n, int32_t 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
   const int32_t wide_dt = hp->ns_precision == DMUON_NS_PREC_BF16 ? DT_BF16 : DT_F32;
-  st = stage_table(ws, P.table_bytes, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("sharded").put_str(P.key).put(io_dtype);
+  for (size_t j = 0; j < sh.size(); ++j) key.put(*sh[j]).put(owner[j]);
+  st = stage_table(ws, P.table_bytes, stream, key.s, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host + P.off_ewmats);
     for (int j = 0; j < P.n; ++j) {
       const MatLayout& L = P.mats[j];
@@ -1555,7 +1690,11 @@ static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, con
   std::vector<int> order(n);
   for (int i = 0; i < n; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return grads[a].bucket < grads[b].bucket; });
-  st = stage_table(ws, L.off_partials, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("clip").put(n).put(nbuckets);
+  for (int i = 0; i < n; ++i) key.put(grads[i]);
+  for (int b = 0; b < nbuckets; ++b) key.put(max_norm[b]);
+  st = stage_table(ws, L.off_partials, stream, key.s, [&](char* host) {
     ClipItem* items = reinterpret_cast<ClipItem*>(host + L.off_items);
     int64_t* bb = reinterpret_cast<int64_t*>(host + L.off_bucket_blocks);
     double* mx = reinterpret_cast<double*>(host + L.off_max_norm);
@@ -1670,7 +1809,11 @@ int dmuon_adamw_step(const dmuon_adamw_tensor_t* tensors, int32_t n, const dmuon
   if (st) return st;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   int64_t blocks = 0, bytes = 0;
-  st = stage_table(workspace, need, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("adamw").put(ngroups);
+  for (int i : active) key.put(tensors[i]);
+  for (int k = 0; k < ngroups; ++k) key.put(groups[k]);
+  st = stage_table(workspace, need, stream, key.s, [&](char* host) {
     AdamItem* items = reinterpret_cast<AdamItem*>(host);
     for (size_t j = 0; j < active.size(); ++j) {
       const dmuon_adamw_tensor_t& T = tensors[active[j]];
@@ -1743,7 +1886,10 @@ int dmuon_apply_update(const dmuon_matrix_t* mats, int32_t n, const void* const*
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   char* ws = static_cast<char*>(workspace);
   const float decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
-  st = stage_table(ws, sizeof(EwMat) * n, stream, [&](char* host) {
+  KeyBuf key;
+  key.put_str("apply_update").put(update_dtype).put(hp->lr).put(hp->weight_decay);
+  for (int j = 0; j < n; ++j) key.put(mats[j]).put(update[j]);
+  st = stage_table(ws, sizeof(EwMat) * n, stream, key.s, [&](char* host) {
     EwMat* em = reinterpret_cast<EwMat*>(host);
     for (int j = 0; j < n; ++j) {
       const dmuon_matrix_t& m = mats[j];

@@ -186,23 +186,21 @@ __device__ __forceinline__ void lds_barrier() {
 // read per cycle: 16 consecutive rows, one chunk) then covers all 64 banks.
 __device__ __forceinline__ int slot_of(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-// Buffer load into LDS (the LLVM intrinsic: descriptor, LDS address, bytes
-// per lane, per-lane offset, wave offset, immediate offset, cache bits).
-// Lane l writes bytes 16l..16l+15 of a 1 KB block at the LDS address; a lane
-// whose offset is outside the descriptor's range reads zeros.
-__device__ void raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* lds, int size, int voffset, int soffset,
-                                    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-// raw buffer descriptor (gfx9 layout): 48-bit base address, no stride,
-// `bytes` in range, default format word
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, int bytes) {
+// Buffer descriptor of one operand slab (gfx9 raw buffer: 48-bit base, no
+// stride, `bytes` in range, default format word); a lane whose offset is
+// outside the range reads zeros.  Base and range are made wave-uniform so
+// the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(a)));
-  r[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  return r;
+  const uint64_t u = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32))))) << 32) |
+                     uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a))));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(u), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+// Buffer load into LDS: lane l writes bytes 16l..16l+15 of the 1 KB block
+// at `lds`, read from the descriptor's base + voffset.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, LDS_AS void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds, 16, voffset, 0, 0, 0);
 }
 
 template <int BT, int kStages>
@@ -347,12 +345,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // part h of stage `data`'s loads into ring slot `slot % kStages`
   auto issue_part = [&](int data, int slot, int h) {
     char* st = smem + (slot % kStages) * STB;
-    const i32x4_t ra = make_rsrc(a_base + data * kRowBytes, a_span);
-    const i32x4_t rb = make_rsrc(b_base + data * kRowBytes, b_span);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + data * kRowBytes, a_span);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + data * kRowBytes, b_span);
 #pragma unroll
     for (int q = h ? LQ3 : 0; q < (h ? LOADS : LQ3); ++q)
-      raw_buffer_load_lds(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(st + dst_off[q]), 16,
-                          int(voff[q]), 0, 0, 0);
+      buffer_load_lds16(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(st + dst_off[q]), int(voff[q]));
   };
   // MFMAs of one quarter with the next quarter's reads and part of a stage's
   // loads interleaved; the reads come first in program order (the compiler

@@ -16,5 +16,4 @@ from .muon import (  # noqa: F401
     apply_update,
     round_to_bf16,
     muon_step,
-    ns_flops_nominal,
 )

@@ -176,8 +176,3 @@ def muon_step(w, grad, buf, *, lr=0.02, momentum=0.95, nesterov=True,
         w_new = round_to_bf16(w_new)
     return w_new, buf_new, u, o
 
-
-def ns_flops_nominal(rows: int, cols: int, ns_steps: int = 5) -> float:
-    """Metric flop count: 4 m^2 n + 2 m^3 per iteration with m <= n."""
-    m, n = min(rows, cols), max(rows, cols)
-    return float(ns_steps) * (4.0 * m * m * n + 2.0 * m ** 3)

@@ -202,6 +202,56 @@ def test_plan_tile_choice(dm):
     assert p4m["matrices"][-1]["tile"] == 64 and {l["tile"] for l in p4m["launches"]} == {64, 128}
 
 
+def _tile_from_info(info, shapes, prec):
+    """The tile edge the rule stated by dmuon_backend_info picks for a batch."""
+    if prec == "bf16":
+        g = info["ns_gemm_bf16"]
+        rule = g["big_tile_rule"]
+        small, big = g["tiles"]
+        tiles = wide = 0
+        for r, c in shapes:
+            t = -(-min(r, c) // big)
+            tiles += t * (t + 1) // 2
+            if min(r, c) >= rule["wide_min_dim"]:
+                wide += t * (t + 1) // 2
+        use_big = tiles >= rule["min_first_stage_tiles"] and wide >= rule["min_wide_share"] * tiles
+    else:
+        g = info["ns_gemm_f32"]
+        rule = g["big_tile_rule"]
+        small, big = g["tiles"]
+        tiles = 0
+        for r, c in shapes:
+            t = -(-min(r, c) // big)
+            tiles += t * (t + 1) // 2
+        use_big = tiles >= rule["min_first_stage_tiles"]
+    per_matrix = [big if use_big and min(r, c) >= rule["min_matrix_dim"] else small for r, c in shapes]
+    return (big if use_big else small), per_matrix
+
+
+def test_backend_info_describes_the_plan(dm, monkeypatch):
+    """dmuon_backend_info states the kernels' tile edges and the rule that
+    picks them; the planner's choice for every workload and precision is the
+    one that rule gives."""
+    import dmuon_inputs as di
+    monkeypatch.delenv("DMUON_GEMM_TILE", raising=False)
+    monkeypatch.delenv("DMUON_GEMM_TILE_F32", raising=False)
+    info = dm.dmuon_backend_info()
+    assert info["ns_gemm_bf16"]["mfma"] == "v_mfma_f32_32x32x16_bf16"
+    assert info["ns_gemm_f32"]["mfma"] == "v_mfma_f32_32x32x2f32"
+    batches = [[(m.rows, m.cols) for m in di.workload(k).matrices] for k in range(5)]
+    batches += [[(3072, 8192)], [(1024, 1024)] * 16, [(4096, 4096)], [(128, 2048)] * 40,
+                [(m.rows, m.cols) for m in di.workload(2).matrices] + [(128, 2048)]]
+    for shapes in batches:
+        for prec in ("bf16", "f32"):
+            plan = dm.dmuon_plan_describe(shapes, ns_precision=prec)
+            tile, per = _tile_from_info(info, shapes, prec)
+            assert plan["tile"] == tile, (len(shapes), prec)
+            assert [m["tile"] for m in plan["matrices"]] == per, (len(shapes), prec)
+            assert {l["tile"] for l in plan["launches"]} <= set(info["ns_gemm_" + prec]["tiles"])
+    env = info["tile_override_env"]
+    assert (env["bf16"], env["f32"]) == ("DMUON_GEMM_TILE", "DMUON_GEMM_TILE_F32")
+
+
 def test_plan_tile_override(dm, monkeypatch):
     """DMUON_GEMM_TILE / DMUON_GEMM_TILE_F32 force the tile edge of their
     precision only."""

@@ -6,8 +6,6 @@ Parity measures (relative Frobenius error):
   momentum buffer after every step        <= 1e-6
   parameter change W_new - W_old          <= 2e-2 (bf16 NS) / 1e-4 (fp32 NS)
 """
-import time
-
 import numpy as np
 import pytest
 import torch
@@ -75,20 +73,20 @@ RAGGED_SPECS = {
 @pytest.mark.parametrize("batch", ["mixed", "bf16"])
 @pytest.mark.parametrize("prec", ["bf16", "f32"])
 def test_step_ragged_multi_step(lib, prec, gemm_tile, batch):
-    """A batch of differently shaped matrices over three steps; the oracle
-    runs its own trajectory (its own parameters and momenta, rounded to the
-    parameter dtype each step) from the same start and gradients.  Checked
-    after every step: the momentum (relative error <= 1e-6) and the change of
-    each parameter since the start, within the NS tolerance plus the
-    parameter roundings of both trajectories (one bf16 ulp per step)."""
+    """A batch of differently shaped matrices over three steps.  Checked
+    after every step: the momentum against the oracle's own recurrence
+    (relative error <= 1e-6), and each parameter against the oracle's update
+    of the GPU's own parameter before the step with the oracle's NS output
+    of the oracle's own NS input: fp32 parameters to the NS tolerance, bf16
+    parameters to the NS tolerance plus half a bf16 ulp of the result (the
+    one rounding of the step), and with fp32 products every element within
+    one bf16 ulp of the oracle's rounded value (99 % equal)."""
     specs = RAGGED_SPECS[batch]
     rng = np.random.default_rng(11)
-    params, w0, moms, m_ref, w_ref = [], [], [], [], []
+    params, moms, m_ref = [], [], []
     for i, (r, c, dt) in enumerate(specs):
-        raw, x = di.normal_matrix(r, c, 0.02, dt, seed=0, tag=(20, i))
+        raw, _ = di.normal_matrix(r, c, 0.02, dt, seed=0, tag=(20, i))
         params.append(upload(raw, dt))
-        w0.append(x)
-        w_ref.append(x.copy())
         moms.append(torch.zeros(r, c, dtype=torch.float32, device=DEV))
         m_ref.append(np.zeros((r, c)))
     hp = dict(lr=0.02, momentum=0.95, nesterov=True, ns_steps=5, weight_decay=0.1,
@@ -97,22 +95,45 @@ def test_step_ragged_multi_step(lib, prec, gemm_tile, batch):
         gs = [di.normal_matrix(r, c, 1e-3 * float(np.exp(rng.standard_normal())), dt, seed=0,
                                tag=(21, i, step)) for i, (r, c, dt) in enumerate(specs)]
         grads = [upload(raw, dt) for (raw, _), (_, _, dt) in zip(gs, specs)]
+        w_old = [f64(p) for p in params]
         lib.dmuon_step(params, grads, moms, **hp)
         torch.cuda.synchronize()
         for i, (r, c, dt) in enumerate(specs):
-            w_ref[i], m_ref[i], _, _ = orc.muon_step(w_ref[i], gs[i][1], m_ref[i], ns_backend="gram",
-                                                     weight_decay=0.1, param_dtype=dt)
+            w_ref, m_ref[i], _, _ = orc.muon_step(w_old[i], gs[i][1], m_ref[i], ns_backend="gram",
+                                                  weight_decay=0.1, param_dtype="f32")
             assert rel(f64(moms[i]), m_ref[i]) <= 1e-6, (step, i)
             got = f64(params[i])
-            d_ref = w_ref[i] - w0[i]
-            err = rel(got - w0[i], d_ref)
-            allow = 0.0
-            if dt == "bf16":
-                allow = (step + 1) * float(np.linalg.norm(bf16_ulp(got)) / np.linalg.norm(d_ref))
-            assert err <= NS_TOL[prec] + allow, (step, i, (r, c), err, allow)
             assert np.isfinite(got).all()
-            print(f"step {step} {r}x{c} {dt} ns={prec} tile={gemm_tile}: change rel err {err:.3e} "
-                  f"(rounding allowance {allow:.1e})")
+            err = check_param_step(got, w_old[i], w_ref, dt, NS_TOL[prec], prec,
+                                   what=f"step {step} {r}x{c} {dt}")
+            print(f"step {step} {r}x{c} {dt} ns={prec} tile={gemm_tile}: update rel err {err:.3e}")
+
+
+def test_step_on_side_stream(lib):
+    """A step on a stream other than the current one, with the workspace
+    allocated by the binding, while the current stream allocates and writes
+    memory before anything waits for the step: the result is bit-identical
+    to the same step on the current stream."""
+    shapes = [(2048, 8192), (8192, 2048), (3072, 3072), (1024, 4096)]
+    def init():
+        ps = [upload(di.normal_matrix(r, c, 0.02, "bf16", 0, (50, i))[0], "bf16") for i, (r, c) in enumerate(shapes)]
+        ms = [torch.zeros(r, c, dtype=torch.float32, device=DEV) for r, c in shapes]
+        return ps, ms
+    grads = [upload(di.normal_matrix(r, c, 1e-3, "bf16", 0, (51, i))[0], "bf16") for i, (r, c) in enumerate(shapes)]
+    pa, ma = init()
+    lib.dmuon_step(pa, grads, ma)
+    torch.cuda.synchronize()
+    nbytes = lib.dmuon_step_workspace_size(pa, grads, ma)
+    pb, mb = init()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    lib.dmuon_step(pb, grads, mb, stream=side)       # workspace allocated by the binding
+    junk = [torch.full((nbytes // 4 + 4096,), 7, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del junk
+    for i in range(len(shapes)):
+        assert torch.equal(pa[i], pb[i]) and torch.equal(ma[i], mb[i]), i
 
 
 def test_step_nan_isolation_and_skip(lib):
@@ -173,29 +194,3 @@ def test_step_deterministic_and_resume(lib, prec, gemm_tile):
     for i in range(len(shapes)):
         assert torch.equal(pa[i], pb[i]) and torch.equal(ma[i], mb[i])
         assert torch.equal(pa[i], pd[i]) and torch.equal(ma[i], md[i])
-
-
-def test_step_decoder_layer_full_size(lib):
-    """The 3B decoder layer's seven projections at full size: one step checked
-    in full against the oracle; momentum checked over ten steps."""
-    w = di.workload(1)
-    idx = list(range(len(w.matrices)))
-    params, w0, moms = _state(w, idx)
-    m_ref = [np.zeros((m.rows, m.cols)) for m in w.matrices]
-    for step in range(w.steps):
-        grads, g = _grads(w, idx, step)
-        lib.dmuon_step(params, grads, moms, **w.hparams())
-        torch.cuda.synchronize()
-        for i in idx:
-            m_ref[i], _ = orc.momentum_update(m_ref[i], g[i], w.momentum, w.nesterov)
-            assert rel(f64(moms[i]), m_ref[i]) <= 1e-6, (step, i)
-        if step == 0:
-            t0 = time.time()
-            for i in idx:
-                w_ref, _, _, _ = orc.muon_step(w0[i], g[i], np.zeros_like(g[i]),
-                                               ns_backend="gram", param_dtype="f32")
-                err = check_param_step(f64(params[i]), w0[i], w_ref, "bf16", NS_TOL["bf16"],
-                                       "bf16", what=w.matrices[i].name)
-                print(f"{w.matrices[i].name} {w.matrices[i].rows}x{w.matrices[i].cols}: "
-                      f"update rel err {err:.3e}", flush=True)
-            print(f"oracle time {time.time() - t0:.1f}s", flush=True)
