@@ -279,6 +279,30 @@ int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dmuon_clip_grad_norm for callers that cannot allocate device or pinned
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments and results as dmuon_clip_grad_norm,
+ * without the workspace: the clip's scratch (gradient table, per-bucket block
+ * ranges and max_norm values, one fp64 partial per 64 KB of gradient, the
+ * per-bucket coefficients) lives in a device array the library holds on each
+ * GPU until the process ends, DMUON_NOALLOC_SCRATCH_BYTES long (4 MiB: about
+ * 30 GB of gradients with few buckets), and the table reaches it as the
+ * arguments of small copy kernels.  The call allocates nothing (no hipMalloc,
+ * hipHostMalloc, event or stream creation); its first call on a device looks
+ * the array's address up once.
+ * Errors as dmuon_clip_grad_norm, and DMUON_ERR_WORKSPACE, before any
+ * launch, when the gradients need more scratch than the array holds
+ * (dmuon_clip_workspace_size > DMUON_NOALLOC_SCRATCH_BYTES).
+ * Every call on one GPU uses the same array: calls that overlap on one GPU
+ * (on different streams, or enqueued from several threads without ordering)
+ * race on it.  Calls in one stream are ordered and safe.
+ */
+#define DMUON_NOALLOC_SCRATCH_BYTES (4u << 20)
+int dmuon_clip_grad_norm_noalloc(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets,
+                                 const double* max_norm, double norm_type, double* total_norm,
+                                 void* stream);
+
+/*
  * The clip's norms and coefficients without the scaling pass: coef_out
  * (device, nbuckets doubles, required) receives coef_b; the gradients are
  * only read.  For dmuon_step_scaled.  Arguments, workspace and errors as

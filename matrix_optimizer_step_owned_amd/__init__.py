@@ -115,6 +115,8 @@ EXPORTS = {
     "dmuon_clip_grad_norm": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P,
                                             ctypes.c_size_t, _P]),
+    "dmuon_clip_grad_norm_noalloc": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P]),
     "dmuon_clip_coefficients": (ctypes.c_int, [ctypes.POINTER(dmuon_grad_t), ctypes.c_int32, ctypes.c_int32,
                                                ctypes.POINTER(ctypes.c_double), ctypes.c_double, _P, _P, _P,
                                                ctypes.c_size_t, _P]),
@@ -568,6 +570,49 @@ def dmuon_clip_grad_norm(grads: List[torch.Tensor], max_norm, *, norm_type: floa
     _check(_lib.dmuon_clip_grad_norm(arr, n, nb, mx, float(norm_type), total_norm.data_ptr(),
                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream, device)),
            "dmuon_clip_grad_norm")
+    return total_norm
+
+
+DMUON_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def _grad_descs(grads, buckets):
+    arr = (dmuon_grad_t * max(len(grads), 1))()
+    for i, g in enumerate(grads):
+        if not g.is_contiguous():
+            raise ValueError(f"grads[{i}] must be contiguous")
+        arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = g.numel(), g.data_ptr(), _dtype(g), int(buckets[i])
+    return arr
+
+
+def dmuon_clip_grad_norm_noalloc(grads: List[torch.Tensor], max_norm, *, norm_type: float = 2.0,
+                                 buckets: Optional[Sequence[int]] = None,
+                                 total_norm: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """dmuon_clip_grad_norm without a workspace and without any allocation:
+    the library's per-GPU scratch array holds the clip's scratch.  The
+    per-bucket totals go to ``total_norm`` (a float64 device tensor of one
+    entry per bucket) if given, and are returned; nothing is allocated
+    here either."""
+    n = len(grads)
+    if buckets is None:
+        buckets = [0] * n
+    if len(buckets) != n:
+        raise ValueError("buckets must have one entry per gradient")
+    nb = (max(buckets) + 1) if n else 1
+    if isinstance(max_norm, (int, float)):
+        max_norm = [float(max_norm)] * nb
+    nb = max(nb, len(max_norm))
+    if len(max_norm) != nb:
+        raise ValueError("max_norm must have one value per bucket")
+    if total_norm is not None and (total_norm.dtype != torch.float64 or total_norm.numel() < nb):
+        raise ValueError("total_norm must be a float64 tensor of one entry per bucket")
+    if n == 0:
+        return total_norm
+    arr = _grad_descs(grads, buckets)
+    mx = (ctypes.c_double * nb)(*[float(v) for v in max_norm])
+    _check(_lib.dmuon_clip_grad_norm_noalloc(arr, n, nb, mx, float(norm_type),
+                                             total_norm.data_ptr() if total_norm is not None else None,
+                                             _stream(stream, grads[0].device)), "dmuon_clip_grad_norm_noalloc")
     return total_norm
 
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdmuon.so")
-SOURCES = ["api.hip", "elementwise.hip", "gemm.hip", "clip.hip", "owners.hip", "adamw.hip"]
+SOURCES = ["api.hip", "elementwise.hip", "gemm.hip", "clip.hip", "owners.hip", "adamw.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -1644,9 +1644,12 @@ size_t dmuon_clip_workspace_size(const dmuon_grad_t* grads, int32_t n, int32_t n
   return clip_layout(grads, n, nbuckets).total;
 }
 
+// noalloc: the workspace is the library's scratch array (dmuon_clip_grad_norm_noalloc);
+// then the table goes up as kernel arguments and no event is created.
 static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
                      double norm_type, double* total_norm, double* coef_out, void* workspace,
-                     size_t workspace_bytes, void* stream_) {
+                     size_t workspace_bytes, void* stream_, bool noalloc = false,
+                     int (*scratch_of_device)(void**) = nullptr) {
   g_last_error.clear();
   if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
   if (nbuckets <= 0) return fail(DMUON_ERR_INVALID_ARG, "nbuckets must be >= 1");
@@ -1669,6 +1672,18 @@ static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, con
   }
   if (n == 0) return DMUON_OK;
   const ClipLayout L = clip_layout(grads, n, nbuckets);
+  if (noalloc && L.total > workspace_bytes) {
+    char buf[192];
+    std::snprintf(buf, sizeof buf,
+                  "these gradients need %zu bytes of clip scratch; the allocation-free entry point holds %zu",
+                  L.total, workspace_bytes);
+    return fail(DMUON_ERR_WORKSPACE, buf);
+  }
+  if (noalloc) {
+    // every host-side check has passed: now the current device's scratch
+    const int sst = scratch_of_device(&workspace);
+    if (sst != DMUON_OK) return sst;
+  }
   if (!workspace || workspace_bytes < L.total) return fail(DMUON_ERR_WORKSPACE, "workspace too small");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(DMUON_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -1690,11 +1705,7 @@ static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, con
   std::vector<int> order(n);
   for (int i = 0; i < n; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return grads[a].bucket < grads[b].bucket; });
-  KeyBuf key;
-  key.put_str("clip").put(n).put(nbuckets);
-  for (int i = 0; i < n; ++i) key.put(grads[i]);
-  for (int b = 0; b < nbuckets; ++b) key.put(max_norm[b]);
-  st = stage_table(ws, L.off_partials, stream, key.s, [&](char* host) {
+  auto fill = [&](char* host) {
     ClipItem* items = reinterpret_cast<ClipItem*>(host + L.off_items);
     int64_t* bb = reinterpret_cast<int64_t*>(host + L.off_bucket_blocks);
     double* mx = reinterpret_cast<double*>(host + L.off_max_norm);
@@ -1712,11 +1723,31 @@ static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, con
       bb[b] = blk;
     }
     for (int b = 0; b < nbuckets; ++b) mx[b] = max_norm[b];
-  });
-  if (st) return st;
+  };
   const ClipItem* items_dev = reinterpret_cast<const ClipItem*>(ws + L.off_items);
   double* partials = reinterpret_cast<double*>(ws + L.off_partials);
   double* coefs = coef_out ? coef_out : reinterpret_cast<double*>(ws + L.off_coefs);
+  if (noalloc) {
+    // the table is written in full here: nothing in the scratch has to
+    // start at zero (every partial and coefficient is written by a kernel)
+    thread_local std::vector<char> host;
+    if (host.size() < L.off_partials) host.resize(L.off_partials);
+    std::memset(host.data(), 0, L.off_partials);
+    fill(host.data());
+    DMUON_HIP_TRY(upload_by_kernel_args(ws, host.data(), L.off_partials, stream));
+    DMUON_HIP_TRY(launch_clip_norm(items_dev, n, L.blocks, norm_type, partials, stream));
+    DMUON_HIP_TRY(launch_clip_finalize(reinterpret_cast<const int64_t*>(ws + L.off_bucket_blocks), nbuckets,
+                                       reinterpret_cast<const double*>(ws + L.off_max_norm), partials, norm_type,
+                                       total_norm, coefs, stream));
+    DMUON_HIP_TRY(launch_clip_scale(items_dev, n, L.blocks, coefs, stream));
+    return DMUON_OK;
+  }
+  KeyBuf key;
+  key.put_str("clip").put(n).put(nbuckets);
+  for (int i = 0; i < n; ++i) key.put(grads[i]);
+  for (int b = 0; b < nbuckets; ++b) key.put(max_norm[b]);
+  st = stage_table(ws, L.off_partials, stream, key.s, fill);
+  if (st) return st;
   int64_t bytes = 0;
   for (int i = 0; i < n; ++i) bytes += grads[i].numel * int64_t(dtype_size(grads[i].dtype));
   DMUON_HIP_TRY(prof_launch(PK_CLIP_NORM, 0, bytes, stream, [&] {
@@ -1733,6 +1764,19 @@ static int clip_impl(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, con
   }));
   return DMUON_OK;
 }
+
+}  // extern "C"
+
+namespace dmuon {
+int clip_grad_norm_in_scratch(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                              double norm_type, double* total_norm, int (*scratch_of_device)(void**),
+                              size_t scratch_bytes, void* stream) {
+  return clip_impl(grads, n, nbuckets, max_norm, norm_type, total_norm, nullptr, nullptr, scratch_bytes, stream,
+                   true, scratch_of_device);
+}
+}  // namespace dmuon
+
+extern "C" {
 
 int dmuon_clip_grad_norm(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
                          double norm_type, double* total_norm, void* workspace, size_t workspace_bytes,

@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <string>
 
+#include "../../include/dmuon.h"
+
 namespace dmuon {
 
 enum : int32_t { DT_F32 = 0, DT_BF16 = 1 };
@@ -206,6 +208,20 @@ hipError_t launch_clip_finalize(const int64_t* bucket_blocks_dev, int nbuckets, 
                                 hipStream_t stream);
 hipError_t launch_clip_scale(const ClipItem* items_dev, int n, int64_t nblocks, const double* coefs,
                              hipStream_t stream);
+
+// Copies `bytes` (a multiple of 16) of host table to device `dst` (16-byte
+// aligned) on `stream` as the arguments of small kernels, kArgChunkBytes per
+// launch: no pinned buffer, no host-memory copy, nothing allocated.
+constexpr int kArgChunkBytes = 2048;
+hipError_t upload_by_kernel_args(void* dst, const void* host, size_t bytes, hipStream_t stream);
+
+// dmuon_clip_grad_norm with the current device's scratch array
+// (scratch_bytes long, its address from scratch_of_device, asked for once
+// every host-side check has passed) as its workspace and its table uploaded
+// by upload_by_kernel_args.
+int clip_grad_norm_in_scratch(const dmuon_grad_t* grads, int32_t n, int32_t nbuckets, const double* max_norm,
+                              double norm_type, double* total_norm, int (*scratch_of_device)(void**),
+                              size_t scratch_bytes, void* stream);
 
 // Tile edges of the grouped GEMM kernels.
 constexpr int kTileBf16 = 128;

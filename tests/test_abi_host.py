@@ -321,6 +321,46 @@ def test_clip_argument_errors_before_launch(dm):
     assert call(ok, 0, ws=None, wsb=0) == dm.DMUON_OK                                    # nothing to do
 
 
+def test_clip_noalloc_errors_before_launch(dm):
+    """The allocation-free clip checks its arguments, and that the gradients
+    fit its fixed scratch, before it looks anything up on a device (the fake
+    device addresses are never dereferenced)."""
+    lib = dm._lib
+    assert dm.DMUON_NOALLOC_SCRATCH_BYTES == 4 << 20
+
+    def grads(specs):
+        arr = (dm.dmuon_grad_t * len(specs))()
+        base = 1 << 41
+        for i, (numel, dt, bucket) in enumerate(specs):
+            arr[i].numel, arr[i].grad, arr[i].dtype, arr[i].bucket = numel, base + i * (1 << 36), dt, bucket
+        return arr
+
+    def call(g, n, nb=1, mx=(1.0,), p=2.0):
+        m = (ctypes.c_double * len(mx))(*mx)
+        return lib.dmuon_clip_grad_norm_noalloc(g, n, nb, m, p, None, None)
+
+    ok = grads([(1000, dm.DMUON_BF16, 0)])
+    assert call(ok, -1) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 1, nb=0) == dm.DMUON_ERR_INVALID_ARG
+    assert call(ok, 1, p=0.0) == dm.DMUON_ERR_INVALID_ARG
+    assert call(grads([(10, 5, 0)]), 1) == dm.DMUON_ERR_UNSUPPORTED
+    assert call(ok, 0) == dm.DMUON_OK
+    # the largest bf16 gradient (in 64 KB chunks) whose scratch fits, then one chunk more
+    def need(chunks):
+        return lib.dmuon_clip_workspace_size(grads([(chunks * 32768, dm.DMUON_BF16, 0)]), 1, 1)
+    lo, hi = 1, 1 << 21
+    while lo + 1 < hi:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if need(mid) <= dm.DMUON_NOALLOC_SCRATCH_BYTES else (lo, mid)
+    assert need(lo) <= dm.DMUON_NOALLOC_SCRATCH_BYTES < need(lo + 1)
+    assert lo * 65536 > 30 * 10**9            # about 30 GB of gradients in one bucket
+    big = grads([((lo + 1) * 32768, dm.DMUON_BF16, 0)])
+    assert call(big, 1) == dm.DMUON_ERR_WORKSPACE
+    assert "scratch" in dm.dmuon_last_error()
+    many = grads([(100, dm.DMUON_F32, 0)] * 140000)      # the gradient table alone is too large
+    assert call(many, 140000) == dm.DMUON_ERR_WORKSPACE
+
+
 def test_sharded_argument_errors_before_launch(dm):
     """Every argument check of the sharded entry point runs before anything
     touches a device (fake device addresses are never dereferenced)."""
