@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--ns-backend", default="gram", choices=["gram", "direct"])
     ap.add_argument("--ns-precision", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-standard-form", action="store_true",
+                    help="time only the chosen form (the default run also times the standard form)")
     ap.add_argument("--cpu-sample", default="auto",
                     help="'auto' (one matrix of each distinct shape) or 'none'")
     ap.add_argument("--copy-probe", action="store_true",
@@ -173,6 +175,24 @@ def read_traffic(summary=TRAFFIC_SUMMARY, source=GEMM_SOURCE):
     if not m_sha or not m_val or m_sha.group(1) != source_sha256(source):
         return None
     return float(m_val.group(1))
+
+
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_3b_stack_mfma_counters.md")
+
+
+def read_mfma_counters(summary=MFMA_SUMMARY, source=GEMM_SOURCE):
+    """Executed MFMA flops per step of the GEMM from the committed counter
+    summary, if it was taken on the current GEMM source; else None."""
+    try:
+        with open(summary) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"executed MFMA flops per step[^:]*:\s*([0-9.]+)\s*TFLOP", text)
+    if not m_sha or not m_val or m_sha.group(1) != source_sha256(source):
+        return None
+    return float(m_val.group(1)) * 1e12
 
 
 def nominal_flops(shapes, ns_steps):
@@ -339,50 +359,61 @@ def main():
             di.torch_normal_(t, w.grad_std, seed=100000 * (s + 1) + i)
             gs.append(t)
         grad_sets.append(gs)
-    ws_bytes = dm.dmuon_step_workspace_size(params, grad_sets[0], moms, **hp)
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    torch.cuda.synchronize()
-    print(f"# workload {w.name}: {len(shapes)} matrices, {w.numel / 1e9:.3f} G elements, "
-          f"workspace {ws_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
-
-    for s in range(args.warmup):
-        dm.dmuon_step(params, grad_sets[s % n_grad_sets], moms, workspace=workspace, **hp)
-    torch.cuda.synchronize()
-    print("# warmup done", file=sys.stderr, flush=True)
-
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    dm.dmuon_profile_begin()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for s in range(args.steps):
-        dm.dmuon_step(params, grad_sets[(args.warmup + s) % n_grad_sets], moms, workspace=workspace, **hp)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prof = dm.dmuon_profile_end()["kernels"]
-    ms_total = start.elapsed_time(end)
-    if args.copy_probe:
-        copy_probe(dev)
-    ms_step = ms_total / args.steps
-    print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
-          file=sys.stderr, flush=True)
-
-    flops_step = nominal_flops(shapes, hp["ns_steps"])
-    value = flops_step / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if args.ns_precision == "bf16" else PEAK_F32_TFLOPS
-    gemm = {k: v for k, v in prof.items() if k.startswith("gemm")}
-    ns_ms = sum(v["ms"] for v in gemm.values()) / args.steps
-    exec_flops = sum(v["flops"] for v in gemm.values()) / args.steps
-    dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
-    # algorithmic flops of the step's launches over their summed duration:
-    # the duration-weighted mean over launches of flops / launch time
-    achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
-    # the committed counter summary covers the default configuration only
+    flops_step = nominal_flops(shapes, hp["ns_steps"])
+
+    def timed_run(hp_run, copy_after=False):
+        """Warm-up steps, then the timed steps of one configuration; returns
+        (ms per step, per-kernel profile, wall seconds)."""
+        ws_bytes = dm.dmuon_step_workspace_size(params, grad_sets[0], moms, **hp_run)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        print(f"# workload {w.name} ({hp_run['ns_backend']}/{hp_run['ns_precision']}): {len(shapes)} matrices, "
+              f"{w.numel / 1e9:.3f} G elements, workspace {ws_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+        for s in range(args.warmup):
+            dm.dmuon_step(params, grad_sets[s % n_grad_sets], moms, workspace=workspace, **hp_run)
+        torch.cuda.synchronize()
+        print("# warmup done", file=sys.stderr, flush=True)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        dm.dmuon_profile_begin()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for s in range(args.steps):
+            dm.dmuon_step(params, grad_sets[(args.warmup + s) % n_grad_sets], moms, workspace=workspace, **hp_run)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        prof = dm.dmuon_profile_end()["kernels"]
+        if copy_after:
+            copy_probe(dev)
+        ms_step = start.elapsed_time(end) / args.steps
+        print(f"# timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f})",
+              file=sys.stderr, flush=True)
+        del workspace
+        torch.cuda.empty_cache()
+        return ms_step, prof, wall
+
+    def gemm_summary(prof):
+        """GEMM time and algorithmic flops per step, and the dominant kernel."""
+        gemm = {k: v for k, v in prof.items() if k.startswith("gemm")}
+        ns_ms = sum(v["ms"] for v in gemm.values()) / args.steps
+        alg_flops = sum(v["flops"] for v in gemm.values()) / args.steps
+        dom_name, dom = max(gemm.items(), key=lambda kv: kv[1]["ms"])
+        # algorithmic flops of the step's launches over their summed duration:
+        # the duration-weighted mean over launches of flops / launch time
+        achieved = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+        return ns_ms, alg_flops, dom_name, dom, achieved
+
+    ms_step, prof, wall = timed_run(hp, copy_after=args.copy_probe)
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    ns_ms, alg_flops, dom_name, dom, achieved = gemm_summary(prof)
+    # the committed counter summaries cover the default configuration only
     default_cfg = args.workload == 2 and args.ns_precision == "bf16" and args.ns_backend == "gram"
     traffic = read_traffic() if default_cfg else None
+    counted = read_mfma_counters() if default_cfg else None
     kernels = {k: {"launches_per_step": v["launches"] / args.steps,
                    "ms_per_step": v["ms"] / args.steps,
                    "tflops": (v["flops"] / (v["ms"] * 1e-3) / 1e12) if v["flops"] else None,
@@ -407,18 +438,42 @@ def main():
                    "grad_dtype": w.grad_dtype, "momentum_dtype": "f32"},
         "steps_per_s": 1e3 / ms_step,
         "matrices_per_s": len(shapes) * 1e3 / ms_step,
-        "step_roofline": step_roofline(w, exec_flops, ms_step, peak),
+        "step_roofline": step_roofline(w, alg_flops, ms_step, peak),
+        # the metric's nominal count (4 m^2 n + 2 m^3 per iteration) over the NS launches' time:
+        # a standard-form-equivalent rate, not a fraction of any peak
         "ns_tflops_nominal": flops_step / (ns_ms * 1e-3) / 1e12,
-        "ns_executed_tflops": exec_flops / (ns_ms * 1e-3) / 1e12,
-        "ns_executed_frac_of_peak": exec_flops / (ns_ms * 1e-3) / 1e12 / peak,
+        # flops the planned products need (symmetric results counted once) over the same time
+        "ns_algorithmic_tflops": alg_flops / (ns_ms * 1e-3) / 1e12,
+        "ns_algorithmic_frac_of_peak": alg_flops / (ns_ms * 1e-3) / 1e12 / peak,
         "ns_ms_per_step": ns_ms,
         "kernels": kernels,
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "traffic_unit": "HBM bytes per launch",
                      "launches": dom["launches"], "mean_launch_ms": dom["ms"] / dom["launches"],
+                     "alg_flops_per_launch": dom["flops"] / dom["launches"],
                      "alg_bytes_per_launch": dom["bytes"] / dom["launches"]},
+        # executed MFMA work from the committed rocprofv3 counter summary (same GEMM source only)
+        "mfma_counters": None if counted is None else {
+            "executed_tflop_per_step": counted / 1e12,
+            "executed_tflops": counted / (ns_ms * 1e-3) / 1e12,
+            "frac_of_peak": counted / (ns_ms * 1e-3) / 1e12 / peak,
+            "summary": os.path.relpath(MFMA_SUMMARY, ROOT)},
     }
+    if default_cfg and not args.no_standard_form:
+        # the headline configuration names both NS forms: time the standard form too
+        hp_std = dict(hp, ns_backend="direct")
+        ms_std, prof_std, _ = timed_run(hp_std)
+        ns_ms_s, alg_s, dom_name_s, dom_s, ach_s = gemm_summary(prof_std)
+        out["standard_form"] = {
+            "ns_backend": "direct", "ms_per_step": ms_std, "value": flops_step / (ms_std * 1e-3) / 1e12,
+            "unit": "TFLOP/s", "steps_per_s": 1e3 / ms_std, "matrices_per_s": len(shapes) * 1e3 / ms_std,
+            "ns_ms_per_step": ns_ms_s, "ns_algorithmic_tflops": alg_s / (ns_ms_s * 1e-3) / 1e12,
+            "step_roofline": step_roofline(w, alg_s, ms_std, peak),
+            "roofline": {"bound": "mfma", "kernel": dom_name_s, "achieved": ach_s, "peak": peak,
+                         "unit": "TFLOP/s", "frac": ach_s / peak,
+                         "mean_launch_ms": dom_s["ms"] / dom_s["launches"]},
+            "gram_speedup": ms_std / ms_step}
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, hp)

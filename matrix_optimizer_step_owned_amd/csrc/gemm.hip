@@ -447,11 +447,37 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   if (kt + 1 < nk) stage_step(kt++, std::false_type{}, std::true_type{});
   stage_step(kt, std::true_type{}, std::false_type{});
   };
+  // The wave of the lower-left quadrant of a diagonal tile of a symmetric
+  // product computes nothing: that quadrant lies below the diagonal, and the
+  // epilogue replaces it by the mirror of the upper one.  It issues its share
+  // of the loads and meets every barrier, and leaves the LDS to the other
+  // three waves' fragment reads.
+  auto idle_loop = [&](auto same) {
+    constexpr bool kSame = decltype(same)::value;
+    issue_part(0, 0, 0);
+    if constexpr (!kSame) issue_part(0, 0, 1);
+    issue_part(nk > 1 ? 1 : 0, 1, 0);
+    wait_vmcnt<LQ3>();
+    __builtin_amdgcn_s_barrier();
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      if constexpr (!kSame) issue_part(kt + 1, kt + 1, 1);
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + 2 < nk) issue_part(kt + 2, kt + 2, 0);
+    }
+  };
+  const bool idle = T.sym && tm == tn && wm == 1 && wn == 0;
   // a diagonal tile of a matrix times itself: one operand's rows serve both
-  if (T.A == T.B && tm == tn)
-    main_loop(std::true_type{});
-  else
+  if (T.A == T.B && tm == tn) {
+    if (idle)
+      idle_loop(std::true_type{});
+    else
+      main_loop(std::true_type{});
+  } else if (idle) {
+    idle_loop(std::false_type{});
+  } else {
     main_loop(std::false_type{});
+  }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
 
