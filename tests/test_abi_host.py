@@ -252,6 +252,29 @@ def test_backend_info_describes_the_plan(dm, monkeypatch):
     assert (env["bf16"], env["f32"]) == ("DMUON_GEMM_TILE", "DMUON_GEMM_TILE_F32")
 
 
+def test_stream_groups_for_small_batches(dm):
+    """A bf16 batch whose first NS stage has fewer than 768 tiles of 256 runs
+    as two groups balanced by m^2 n (the second on the library's own
+    stream); larger batches, single matrices and fp32 products keep one."""
+    import dmuon_inputs as di
+    def groups(shapes, **hp):
+        return dm.dmuon_plan_describe(shapes, **hp)["stream_groups"]
+    layer = [(m.rows, m.cols) for m in di.workload(1).matrices]
+    g = groups(layer)
+    assert len(g) == 2 and sorted(g[0] + g[1]) == list(range(7))
+    cost = [min(r, c) ** 2 * max(r, c) for r, c in layer]
+    loads = sorted(sum(cost[i] for i in grp) for grp in g)
+    assert loads[1] - loads[0] <= max(cost)       # the greedy split's bound
+    assert len(groups([(m.rows, m.cols) for m in di.workload(2).matrices])) == 1
+    assert len(groups([(m.rows, m.cols) for m in di.workload(3).matrices])) == 1
+    assert groups([(4096, 4096)]) == [[0]]
+    assert len(groups(layer, ns_precision="f32")) == 1
+    # the workspace of a split batch holds both groups' plans
+    split_ws = dm.dmuon_orthogonalize_workspace_size(layer)
+    whole = dm.dmuon_plan_describe(layer)["workspace_bytes"]
+    assert split_ws >= whole * 0.9
+
+
 def test_plan_tile_override(dm, monkeypatch):
     """DMUON_GEMM_TILE / DMUON_GEMM_TILE_F32 force the tile edge of their
     precision only."""
