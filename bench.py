@@ -55,6 +55,7 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_3b_stack_hbm_traffic
 GEMM_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "gemm.hip")
 CLIP_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "clip_scale_3b_stack_grads_hbm_traffic.md")
 CLIP_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "clip.hip")
+ELEMENTWISE_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "elementwise.hip")
 ADAMW_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "adamw_3b_symmetric_group_hbm_traffic.md")
 ADAMW_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_owned_amd", "csrc", "adamw.hip")
 ADAMW_METRIC = "fused AdamW GB/s (bf16 params and grads, fp32 moments) for a 3B-shaped symmetric group"
@@ -85,6 +86,8 @@ def parse():
                     help="after the timed steps, copy 1 GiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into the traffic summary and exit")
+    ap.add_argument("--pmc-kernel", default="gemm_bf16_kernel", choices=["gemm_bf16_kernel", "momentum_kernel"],
+                    help="with --pmc-summary: the kernel to summarise")
     ap.add_argument("--mfma-summary", nargs=2, metavar=("PMC_DIR", "BENCH_JSON"),
                     help="summarise a rocprofv3 run of MFMA counters (one step) against a bench line and exit")
     ap.add_argument("--clip", action="store_true",
@@ -306,6 +309,18 @@ def main():
                   f"{x['bytes_per_launch'] / 1e9:.4f} GB per launch")
         print(f"- hbm_bytes_per_launch: {tot:.6e}")
         print(f"- clip_source_sha256: {source_sha256(CLIP_SOURCE)}")
+        return
+    if args.pmc_summary and args.pmc_kernel == "momentum_kernel":
+        r = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], 1, kernel="momentum_kernel", per_step=1)
+        tot = r["FETCH_SIZE"]["bytes_per_launch"] + r["WRITE_SIZE"]["bytes_per_launch"]
+        print("# HBM traffic of momentum_kernel, 3B 28-layer stack (workload 2), gram, bf16\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            x = r[c]
+            print(f"- {c}: {x['kib_per_launch']:.6g} KiB per launch (the last step's launch); "
+                  f"1 GiB copy reads {x['copy_kib']:.6g} KiB -> factor {x['factor']:.4f}; "
+                  f"{x['bytes_per_launch'] / 1e9:.4f} GB per launch")
+        print(f"- hbm_bytes_per_launch: {tot:.6e}")
+        print(f"- elementwise_source_sha256: {source_sha256(ELEMENTWISE_SOURCE)}")
         return
     if args.pmc_summary:
         steps = 1
