@@ -407,7 +407,10 @@ const char* dmuon_backend_info(void);
  * every kernel the library enqueues (from any entry point, on its stream) is
  * bracketed by a pair of HIP events.  dmuon_profile_end() waits for those
  * events and writes JSON into buf (as dmuon_plan_describe does): per kernel
- * kind the launch count, summed device time in ms, and the algorithmic flops
+ * kind the launch count, summed device time in ms ("ms"), the time covered
+ * by the union of those launches' intervals ("wall_ms": less than "ms" when
+ * launches on two streams overlap, as a small batch's two stream groups do),
+ * and the algorithmic flops
  * and HBM bytes of those launches (flops of the NS products with the true,
  * unpadded sizes and symmetric products counted once; bytes that an ideal
  * kernel must move).  Returns the JSON length or a negative status.  Called

@@ -2135,22 +2135,47 @@ int64_t dmuon_profile_end(char* buf, size_t buf_len) {
   }
   int64_t count[PK_COUNT] = {}, flops[PK_COUNT] = {}, bytes[PK_COUNT] = {};
   double ms[PK_COUNT] = {};
+  // every launch's interval against the window's first event (events on
+  // different streams of one device share a clock); the union of a kind's
+  // intervals is its wall time when launches on two streams overlap
+  std::vector<std::pair<double, double>> spans[PK_COUNT];
   int status = DMUON_OK;
   for (auto& r : recs) {
-    float t = 0.f;
+    float t = 0.f, t0 = 0.f;
     if (status == DMUON_OK) {
       hipError_t e = hipEventSynchronize(r.b);
+      if (e == hipSuccess) e = hipEventSynchronize(recs.front().a);
       if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t0, recs.front().a, r.a);
       if (e != hipSuccess) status = fail(DMUON_ERR_HIP, std::string("profile events: ") + hipGetErrorString(e));
     }
     count[r.kind] += 1;
     ms[r.kind] += t;
     flops[r.kind] += r.flops;
     bytes[r.kind] += r.bytes;
+    spans[r.kind].emplace_back(double(t0), double(t0) + double(t));
+  }
+  for (auto& r : recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
   }
   if (status != DMUON_OK) return status;
+  double wall[PK_COUNT] = {};
+  for (int k = 0; k < PK_COUNT; ++k) {
+    auto& v = spans[k];
+    std::sort(v.begin(), v.end());
+    double lo = 0.0, hi = -1.0;
+    for (auto& iv : v) {
+      if (iv.first > hi) {
+        if (hi > lo) wall[k] += hi - lo;
+        lo = iv.first;
+        hi = iv.second;
+      } else {
+        hi = std::max(hi, iv.second);
+      }
+    }
+    if (hi > lo) wall[k] += hi - lo;
+  }
   std::ostringstream os;
   os.precision(9);
   os << "{\"kernels\": {";
@@ -2158,7 +2183,8 @@ int64_t dmuon_profile_end(char* buf, size_t buf_len) {
   for (int k = 0; k < PK_COUNT; ++k) {
     if (!count[k]) continue;
     os << (first ? "" : ", ") << "\"" << kProfNames[k] << "\": {\"launches\": " << count[k]
-       << ", \"ms\": " << ms[k] << ", \"flops\": " << flops[k] << ", \"bytes\": " << bytes[k] << "}";
+       << ", \"ms\": " << ms[k] << ", \"wall_ms\": " << wall[k] << ", \"flops\": " << flops[k]
+       << ", \"bytes\": " << bytes[k] << "}";
     first = false;
   }
   os << "}}";
