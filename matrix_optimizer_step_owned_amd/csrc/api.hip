@@ -808,7 +808,7 @@ int stage_table(void* dst, size_t bytes, hipStream_t stream, const std::string& 
   } else {
     DMUON_HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
   }
-  const hipError_t ce = hipMemcpyAsync(dst, im->host, bytes, hipMemcpyHostToDevice, stream);
+  const hipError_t ce = launch_table_copy(dst, im->host, bytes, stream);
   if (ce != hipSuccess) {
     d->free_events.push_back(ev);
     return fail(DMUON_ERR_HIP, std::string("table copy: ") + hipGetErrorString(ce));
@@ -1106,11 +1106,16 @@ namespace {
 // long-K tiles next to short ones); such a batch (bf16 products, two or more
 // matrices) runs as two groups of matrices, balanced by m^2 n, each with its
 // own launches, the second on a stream of the library's own that forks from
-// and joins back into the caller's stream.  The launch tails of one group
-// then overlap the other group's work.  (Measured on one 3B decoder layer:
-// 3.96 -> 3.71 ms per step; on larger batches two concurrent launch streams
-// were 5-7 % slower, so they keep one.)
+// and joins back into the caller's stream, provided the two groups' loads
+// are within kSplitMaxImbalance of each other.  The launch tails of one
+// group then overlap the other group's work.  Measured per step (50 queued
+// steps): one 3B decoder layer 4.06 -> 3.66 ms; two, four, eight and sixteen
+// equal matrices 4-16 % faster; three and five equal matrices (2:1 and 3:2
+// splits) 7 % and 3 % slower, hence the balance condition; on larger batches
+// two concurrent launch streams were 5-7 % slower, so they keep one.
 constexpr int64_t kSplitMaxTiles = 768;
+constexpr int kStreamGroups = 2;
+constexpr double kSplitMaxImbalance = 1.25;   // heaviest group's m^2 n over the lightest's
 
 struct SplitPlan {
   std::vector<std::vector<int>> groups;          // positions in the active list
@@ -1140,15 +1145,22 @@ std::vector<std::vector<int>> stream_groups(const std::vector<int64_t>& rows, co
     return m * m * nn;
   };
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
-  std::vector<std::vector<int>> two(2);
-  double load[2] = {0.0, 0.0};
+  const int G = std::min(kStreamGroups, n);
+  std::vector<std::vector<int>> gs(G);
+  std::vector<double> load(G, 0.0);
   for (int i : order) {
-    const int k = load[1] < load[0] ? 1 : 0;
-    two[k].push_back(i);
+    int k = 0;
+    for (int j = 1; j < G; ++j)
+      if (load[j] < load[k]) k = j;
+    gs[k].push_back(i);
     load[k] += cost(i);
   }
-  for (auto& v : two) std::sort(v.begin(), v.end());
-  return two;
+  // an uneven split (three or five equal matrices) leaves one stream idle
+  // for a large part of every stage and was measured slower than one stream
+  const auto mm = std::minmax_element(load.begin(), load.end());
+  if (*mm.second > kSplitMaxImbalance * *mm.first) return g;
+  for (auto& v : gs) std::sort(v.begin(), v.end());
+  return gs;
 }
 
 SplitPlan split_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols, int32_t prec,
@@ -1165,46 +1177,56 @@ SplitPlan split_plan(const std::vector<int64_t>& rows, const std::vector<int64_t
   return S;
 }
 
-// The library's second stream on each device and the events that fork it
-// from, and join it back into, the caller's stream.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+// The library's own streams on each device (one per group after the first)
+// and the events that fork them from, and join them back into, the caller's
+// stream (a wait takes an event's latest record at the time of the call, so
+// the same events serve every call).
+struct SideStreams {
+  hipStream_t stream[kStreamGroups - 1] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kStreamGroups - 1] = {};
 };
 std::mutex g_side_mu;
-std::map<int, SideStream> g_side;
+std::map<int, SideStreams> g_side;
 
-int side_stream(SideStream** out) {
+int side_streams(SideStreams** out) {
   int dev = 0;
   DMUON_HIP_TRY(hipGetDevice(&dev));
-  SideStream& s = g_side[dev];
-  if (!s.stream) {
-    DMUON_HIP_TRY(hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking));
+  SideStreams& s = g_side[dev];
+  if (!s.fork) {
+    for (int k = 0; k < kStreamGroups - 1; ++k) {
+      if (!s.stream[k]) DMUON_HIP_TRY(hipStreamCreateWithFlags(&s.stream[k], hipStreamNonBlocking));
+      if (!s.join[k]) DMUON_HIP_TRY(hipEventCreateWithFlags(&s.join[k], hipEventDisableTiming));
+    }
     DMUON_HIP_TRY(hipEventCreateWithFlags(&s.fork, hipEventDisableTiming));
-    DMUON_HIP_TRY(hipEventCreateWithFlags(&s.join, hipEventDisableTiming));
   }
   *out = &s;
   return DMUON_OK;
 }
 
 // Runs run_group(g, stream) for every group: group 0 on the caller's stream,
-// group 1 on the side stream between a fork and a join event.
+// group g > 0 on the library's stream g - 1, between a fork and a join event.
 template <class Run>
 int run_groups(const SplitPlan& S, hipStream_t stream, Run run_group) {
   if (S.groups.size() == 1) return run_group(0, stream);
   std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* side = nullptr;
-  int st = side_stream(&side);
+  SideStreams* side = nullptr;
+  int st = side_streams(&side);
   if (st) return st;
+  const int G = static_cast<int>(S.groups.size());
   DMUON_HIP_TRY(hipEventRecord(side->fork, stream));
-  DMUON_HIP_TRY(hipStreamWaitEvent(side->stream, side->fork, 0));
+  for (int g = 1; g < G; ++g) DMUON_HIP_TRY(hipStreamWaitEvent(side->stream[g - 1], side->fork, 0));
   st = run_group(0, stream);
-  const int st1 = st ? st : run_group(1, side->stream);
-  // the caller's stream waits for the side stream whatever happened above
-  const hipError_t e1 = hipEventRecord(side->join, side->stream);
-  const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(stream, side->join, 0) : e1;
-  if (st1) return st1;
-  if (e2 != hipSuccess) return fail(DMUON_ERR_HIP, std::string("stream join: ") + hipGetErrorString(e2));
+  for (int g = 1; g < G && !st; ++g) st = run_group(g, side->stream[g - 1]);
+  // the caller's stream waits for every group's stream whatever happened above
+  hipError_t ej = hipSuccess;
+  for (int g = 1; g < G; ++g) {
+    hipError_t r = hipEventRecord(side->join[g - 1], side->stream[g - 1]);
+    if (r == hipSuccess) r = hipStreamWaitEvent(stream, side->join[g - 1], 0);
+    if (r != hipSuccess && ej == hipSuccess) ej = r;
+  }
+  if (st) return st;
+  if (ej != hipSuccess) return fail(DMUON_ERR_HIP, std::string("stream join: ") + hipGetErrorString(ej));
   return DMUON_OK;
 }
 

@@ -384,6 +384,31 @@ hipError_t launch_gram_sum(const GramSum* sums_dev, int nsums, int64_t nblocks, 
   return hipGetLastError();
 }
 
+// Launch-table upload: the GPU reads the pinned host image directly (it is
+// mapped into the device's address space) and writes the workspace, 16 bytes
+// per lane, the last bytes one by one.  A kernel on the caller's stream
+// keeps the upload on the compute queue, where waits on other streams are
+// resolved on the GPU; a DMA copy behind such a wait was resolved on the host
+// and blocked it.
+__global__ void __launch_bounds__(256)
+table_copy_kernel(const char* __restrict__ src, char* __restrict__ dst, int64_t bytes) {
+  const int64_t n16 = bytes / 16;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  if (blockIdx.x == 0 && threadIdx.x < bytes - n16 * 16) dst[n16 * 16 + threadIdx.x] = src[n16 * 16 + threadIdx.x];
+}
+
+hipError_t launch_table_copy(void* dst, const void* host_src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  if (reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(host_src) % 16) return hipErrorInvalidValue;
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>(std::max<int64_t>((n16 + 255) / 256, 1), 1024));
+  hipLaunchKernelGGL(table_copy_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const char*>(host_src),
+                     static_cast<char*>(dst), static_cast<int64_t>(bytes));
+  return hipGetLastError();
+}
+
 hipError_t launch_momentum(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode, float mu,
                            int nesterov, float* partials, hipStream_t stream) {
   if (nblocks <= 0) return hipSuccess;

@@ -177,6 +177,9 @@ inline void set_last_error(const char* msg) { set_last_error(0, msg); }
 
 // U = momentum / Nesterov (mode 0) or plain copy (mode 1) of every matrix into
 // its wide buffer; partials[b] = sum of u^2 over block b.
+// Copies `bytes` from a pinned host buffer to device memory with a kernel on
+// `stream` (both 16-byte aligned).
+hipError_t launch_table_copy(void* dst, const void* host_src, size_t bytes, hipStream_t stream);
 hipError_t launch_momentum(const EwMat* mats_dev, int nmats, int64_t nblocks, int mode,
                            float mu, int nesterov, float* partials, hipStream_t stream);
 

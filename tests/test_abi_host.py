@@ -269,6 +269,11 @@ def test_stream_groups_for_small_batches(dm):
     assert len(groups([(m.rows, m.cols) for m in di.workload(3).matrices])) == 1
     assert groups([(4096, 4096)]) == [[0]]
     assert len(groups(layer, ns_precision="f32")) == 1
+    # equal matrices: an even count splits in halves; three (2:1) and five
+    # (3:2) are too uneven and keep one stream
+    assert groups([(3072, 8192)] * 4) == [[0, 2], [1, 3]]
+    assert len(groups([(3072, 3072)] * 3)) == 1
+    assert len(groups([(2048, 8192)] * 5)) == 1
     # the workspace of a split batch holds both groups' plans
     split_ws = dm.dmuon_orthogonalize_workspace_size(layer)
     whole = dm.dmuon_plan_describe(layer)["workspace_bytes"]
