@@ -18,11 +18,18 @@
  *     `stream` (a hipStream_t; NULL is the default stream).  Host structs
  *     and arrays passed in are read before the call returns.
  *   - The caller owns every buffer, including the workspace.  No entry point
- *     allocates or frees device memory.  (The library keeps a small pinned
- *     host staging ring and a shape-keyed plan cache for its own launch
- *     tables.)
+ *     allocates or frees device memory.  (The library keeps pinned host
+ *     images of its launch tables, cached per workspace, plan and pointer
+ *     set, and a shape-keyed plan cache; on each device it creates, once,
+ *     one stream and a few events of its own, which a small batch uses to
+ *     run two groups of matrices concurrently.)
  *   - Calls are asynchronous: results are visible to later work on `stream`.
- *     Calls that share a workspace must be ordered on one stream.
+ *     Calls that share a workspace must be ordered on one stream.  A call
+ *     uploads its launch table into the workspace with a kernel that reads
+ *     the pinned image when it runs, and a later call may refill that image,
+ *     so these entry points must not be captured into a HIP graph for
+ *     replay (dmuon_clip_grad_norm_noalloc, whose tables travel as kernel
+ *     arguments, may be).
  *   - Return value: DMUON_OK, or a negative status.  Every argument check runs
  *     before the first launch, so on an error status nothing was modified.
  *     dmuon_last_error() gives a readable detail for the calling thread.
