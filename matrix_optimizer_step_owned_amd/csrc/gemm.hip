@@ -664,7 +664,8 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // are skipped, and pieces at its edge (or on unaligned rows) go element by
   // element.
   if (Wp) {
-    // eight values: o and w bf16 pairs -> the updated bf16 pairs
+    // eight values: o and w bf16 pairs -> the updated bf16 pairs (rounded
+    // to nearest-even by the packed conversion, as the staging rounds)
     auto update8 = [&](const u32x4_t& o, const u32x4_t& w) {
       u32x4_t r;
 #pragma unroll
@@ -672,7 +673,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
         const float a0 = fmaf(-lr_eff, __uint_as_float(o[k] << 16), __uint_as_float(w[k] << 16) * w_decay);
         const float a1 = fmaf(-lr_eff, __uint_as_float(o[k] & 0xffff0000u),
                               __uint_as_float(w[k] & 0xffff0000u) * w_decay);
-        r[k] = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+        r[k] = pack_bf16x2(a0, a1);
       }
       return r;
     };
