@@ -1104,18 +1104,19 @@ namespace {
 // A batch whose first NS stage has fewer than kSplitMaxTiles tiles of 256
 // leaves most of the chip idle in every launch (fewer than three waves, and
 // long-K tiles next to short ones); such a batch (bf16 products, two or more
-// matrices) runs as two groups of matrices, balanced by m^2 n, each with its
+// matrices) runs as two groups of matrices, balanced by their NS flops, each with its
 // own launches, the second on a stream of the library's own that forks from
 // and joins back into the caller's stream, provided the two groups' loads
 // are within kSplitMaxImbalance of each other.  The launch tails of one
 // group then overlap the other group's work.  Measured per step (50 queued
-// steps): one 3B decoder layer 4.06 -> 3.66 ms; two, four, eight and sixteen
-// equal matrices 4-16 % faster; three and five equal matrices (2:1 and 3:2
-// splits) 7 % and 3 % slower, hence the balance condition; on larger batches
-// two concurrent launch streams were 5-7 % slower, so they keep one.
+// steps): one 3B decoder layer 4.06 -> 3.66 ms (its best split is 1.25:1 in
+// flops); two, four, eight and sixteen equal matrices 4-16 % faster; three
+// and five equal matrices (2:1 and 3:2 splits) 7 % and 3 % slower, hence the
+// balance condition; on larger batches two concurrent launch streams were
+// 5-7 % slower, so they keep one.
 constexpr int64_t kSplitMaxTiles = 768;
 constexpr int kStreamGroups = 2;
-constexpr double kSplitMaxImbalance = 1.25;   // heaviest group's m^2 n over the lightest's
+constexpr double kSplitMaxImbalance = 1.4;    // heaviest group's NS flops over the lightest's
 
 struct SplitPlan {
   std::vector<std::vector<int>> groups;          // positions in the active list
@@ -1124,10 +1125,22 @@ struct SplitPlan {
   size_t ws_bytes = 0;
 };
 
+// Flops of one matrix's NS products with K iterations, symmetric results
+// counted once (the measure the stream groups balance): the standard form
+// runs X X^T (m^2 n), B (m^3) and B X (2 m^2 n) per iteration; the Gram form
+// R (m^2 n), 4K - 3 products of m x m matrices (m^3 each) and O (2 m^2 n).
+double ns_cost(int64_t rows, int64_t cols, int32_t backend, int K) {
+  const double m = double(std::min(rows, cols)), n = double(std::max(rows, cols));
+  if (K == 0) return m * n;
+  if (choose_form(backend, static_cast<int64_t>(m), static_cast<int64_t>(n)) == FORM_DIRECT)
+    return K * (3.0 * m * m * n + m * m * m);
+  return 3.0 * m * m * n + (4.0 * K - 3.0) * m * m * m;
+}
+
 // Groups of the active matrices (rows/cols in active order): one group, or
 // two balanced ones when the batch is small.
 std::vector<std::vector<int>> stream_groups(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols,
-                                            int32_t prec) {
+                                            int32_t prec, int32_t backend, int K) {
   const int n = static_cast<int>(rows.size());
   std::vector<std::vector<int>> g(1);
   for (int i = 0; i < n; ++i) g[0].push_back(i);
@@ -1140,10 +1153,7 @@ std::vector<std::vector<int>> stream_groups(const std::vector<int64_t>& rows, co
   if (tiles >= kSplitMaxTiles) return g;
   std::vector<int> order(n);
   for (int i = 0; i < n; ++i) order[i] = i;
-  auto cost = [&](int i) {
-    const double m = double(std::min(rows[i], cols[i])), nn = double(std::max(rows[i], cols[i]));
-    return m * m * nn;
-  };
+  auto cost = [&](int i) { return ns_cost(rows[i], cols[i], backend, K); };
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
   const int G = std::min(kStreamGroups, n);
   std::vector<std::vector<int>> gs(G);
@@ -1166,7 +1176,7 @@ std::vector<std::vector<int>> stream_groups(const std::vector<int64_t>& rows, co
 SplitPlan split_plan(const std::vector<int64_t>& rows, const std::vector<int64_t>& cols, int32_t prec,
                      int32_t backend, const Coeffs& cf) {
   SplitPlan S;
-  S.groups = stream_groups(rows, cols, prec);
+  S.groups = stream_groups(rows, cols, prec, backend, static_cast<int>(cf.abc.size() / 3));
   for (const auto& g : S.groups) {
     std::vector<int64_t> r, c;
     for (int i : g) { r.push_back(rows[i]); c.push_back(cols[i]); }
@@ -2266,7 +2276,7 @@ int64_t dmuon_plan_describe(const int64_t* rows, const int64_t* cols, int32_t n,
     // the groups dmuon_step / dmuon_orthogonalize run on two streams (one
     // group: a single launch sequence)
     const auto groups = stream_groups(std::vector<int64_t>(rows, rows + n), std::vector<int64_t>(cols, cols + n),
-                                      hp->ns_precision);
+                                      hp->ns_precision, hp->ns_backend, P.ns_steps);
     os << ", \"stream_groups\": [";
     for (size_t g = 0; g < groups.size(); ++g) {
       os << (g ? ", " : "") << "[";

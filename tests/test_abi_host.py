@@ -259,12 +259,19 @@ def test_stream_groups_for_small_batches(dm):
     import dmuon_inputs as di
     def groups(shapes, **hp):
         return dm.dmuon_plan_describe(shapes, **hp)["stream_groups"]
+    def ns_cost(r, c, k=5):
+        # flops of the planned products, symmetric ones counted once
+        m, n = min(r, c), max(r, c)
+        if n < 2 * m:                              # the gram backend's standard form
+            return k * (3 * m * m * n + m ** 3)
+        return 3 * m * m * n + (4 * k - 3) * m ** 3
     layer = [(m.rows, m.cols) for m in di.workload(1).matrices]
     g = groups(layer)
     assert len(g) == 2 and sorted(g[0] + g[1]) == list(range(7))
-    cost = [min(r, c) ** 2 * max(r, c) for r, c in layer]
+    cost = [ns_cost(r, c) for r, c in layer]
     loads = sorted(sum(cost[i] for i in grp) for grp in g)
     assert loads[1] - loads[0] <= max(cost)       # the greedy split's bound
+    assert loads[1] <= 1.4 * loads[0]
     assert len(groups([(m.rows, m.cols) for m in di.workload(2).matrices])) == 1
     assert len(groups([(m.rows, m.cols) for m in di.workload(3).matrices])) == 1
     assert groups([(4096, 4096)]) == [[0]]
