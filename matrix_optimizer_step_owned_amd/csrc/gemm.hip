@@ -25,11 +25,18 @@
 // stage is 128 bytes, one cache line; chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7), which the loads realise by choosing each lane's source
 // address, so that a fragment read (16 rows x one 16-byte chunk per cycle)
-// covers all 64 banks.  A stage runs as four k-quarters; each starts with an
-// MFMA and interleaves the next quarter's fragment reads with its MFMAs; the
-// one barrier per stage sits before the last quarter; the loads of the stage
-// two ahead are split between that last quarter and the next stage's first
-// one; the last two stages are peeled so that nothing is loaded past the end.
+// covers all 64 banks.  A stage runs as four k-quarters of 16 MFMAs per wave.
+// 256-tiles hold four quarters of fragments in registers: a stage's
+// fragments are read within its first quarter and the quarter before, a
+// barrier after that quarter frees its ring slot, and the loads of the stage
+// two ahead go into the slot over the following four quarters, most of them
+// in the two quarters without fragment reads; a second barrier after the
+// third quarter makes the next stage visible (explicit wait counts, no
+// fence, so the loads issued since stay in flight).  128-tiles interleave
+// each quarter's MFMAs with the next quarter's reads, have one barrier per
+// stage before its last quarter, and split the loads of the stage two ahead
+// between that quarter and the next stage's first.  The last two stages are
+// peeled so that nothing is loaded past the end.
 // A diagonal tile of a product of a matrix with itself (A A, X X^T) loads its
 // rows once: the B fragments are read from the A rows (a second instance of
 // the loop, chosen per block).
@@ -136,7 +143,6 @@ __device__ __forceinline__ void store_fragment(const f32x16_t& a, OutT* __restri
 // ---------------------------------------------------------------------------
 
 constexpr int kStageK = 64;                     // k per LDS stage
-constexpr int kLoadsEarly256 = 8;               // of a stage's 16 loads per wave, issued a quarter early
 constexpr int kRowBytes = kStageK * 2;          // 128: one cache line per row
 constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows filled by one wave-wide DMA load
 
@@ -329,6 +335,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   };
 
   // Ring of two stages, 64 k each; stage kt's data sits in slot kt % 2.
+  // 128-tiles (the 256-tile schedule follows below).
   // Per stage: quarters 0-2 run on fragments already in registers while the
   // next quarter's load; then one barrier, at which stage kt+1 has landed
   // (own loads counted, everyone's by the barrier) and every wave has
@@ -340,7 +347,7 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // last stage issues none and has no barrier.
   static_assert(kStages == 2, "two-slot ring");
   // loads of a stage issued in quarter 3 (the rest go in the next quarter 0)
-  constexpr int LQ3 = BT == 256 ? kLoadsEarly256 : LOADS / 2;
+  constexpr int LQ3 = LOADS / 2;
   constexpr int LQ0 = LOADS - LQ3;
   // part h of stage `data`'s loads into ring slot `slot % kStages`
   auto issue_part = [&](int data, int slot, int h) {
@@ -358,42 +365,14 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   // cover a read of the next quarter issued ahead of it)
   auto pin_quarter_with_loads = [&](auto nloads) {
     constexpr int V = decltype(nloads)::value;
-    if constexpr (BT == 256) {           // 16 MFMAs, 8 reads, V loads
+    // (instantiated for 256-tiles too, whose schedule is main_loop4; never run there)
+    static_assert(BT != 128 || (NMFMA == 4 && NFRAG == 4 && (V == 4 || V == 0)), "schedule");
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 1);
-      }
-      if constexpr (V > 12) {
-#pragma unroll
-        for (int i = 0; i < V - 12; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kVmem, 2, 1);
-        }
-#pragma unroll
-        for (int i = 0; i < 24 - V; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-          __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
-        }
-        if constexpr (V < 12) __builtin_amdgcn_sched_group_barrier(kMfma, 12 - V, 1);
-      }
-    } else {                             // 4 MFMAs, 4 reads, 4 or 0 loads
-      static_assert(V == 4 || V == 0, "schedule");
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
-        if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
-      }
+    for (int i = 0; i < 4; ++i) {                  // 4 MFMAs, 4 reads, 4 or 0 loads
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 1);
+      if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kVmem, 1, 1);
     }
-    static_assert(BT == 256 ? (NMFMA == 16 && NFRAG == 8 && V <= 16)
-                            : (NMFMA == 4 && NFRAG == 4), "schedule");
     __builtin_amdgcn_sched_barrier(0);
   };
   auto main_loop = [&](auto same) {
@@ -466,17 +445,234 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       if (kt + 2 < nk) issue_part(kt + 2, kt + 2, 0);
     }
   };
+
+  // 256-tiles: four fragment sets, two barriers per stage.  Set k holds
+  // k-quarter k of a stage.  Stage s+1's quarters 0 and 1 are read during
+  // quarter 3 of stage s (one read behind each MFMA), its quarters 2 and 3
+  // during its own quarter 0 (two behind each of the first eight MFMAs).
+  // After quarter 0 a barrier frees the ring slot of stage s, and stage
+  // s+2's 16 loads per wave go into it: 6 in quarter 1, 6 in quarter 2, 2 in
+  // quarter 3, 2 in quarter 0 of stage s+1, evenly spaced within each
+  // quarter.  After quarter 2 a second barrier makes stage s+1 visible: each
+  // wave first waits for its own loads of that stage, the ones of stage s+2
+  // issued since stay in flight.  Neither barrier carries a memory fence (a
+  // fence would also wait for every direct-to-LDS load); the waits before
+  // them are explicit.
+  constexpr int LP1 = 6, LP2 = 6, LP3 = 2;       // loads per wave in quarters 1, 2, 3; the rest in quarter 0
+  static_assert(BT != 256 || (LOADS == 16 && LP1 + LP2 + LP3 <= LOADS), "schedule");
+  // load position p of a stage -> load q; A (q < 8) and B rows alternate, so
+  // a diagonal tile of a matrix times itself (A rows only) splits its loads
+  // over the four parts in the same proportion
+  auto ord4 = [](int p) constexpr { return (p & 1) ? LOADS / 2 + (p >> 1) : (p >> 1); };
+  auto plo4 = [](int h) constexpr { return h == 1 ? 0 : h == 2 ? LP1 : h == 3 ? LP1 + LP2 : LP1 + LP2 + LP3; };
+  auto phi4 = [](int h) constexpr { return h == 1 ? LP1 : h == 2 ? LP1 + LP2 : h == 3 ? LP1 + LP2 + LP3 : LOADS; };
+  // loads in part h (the quarter that issues them) of one stage
+  auto pcount4 = [ord4, plo4, phi4](auto part, auto same) constexpr {
+    constexpr int H = decltype(part)::value;
+    int n = 0;
+    for (int p = plo4(H); p < phi4(H); ++p) n += (!decltype(same)::value || ord4(p) < LOADS_PER_OP / 4) ? 1 : 0;
+    return n;
+  };
+  // q of the l-th load of part h
+  auto pq4 = [ord4, plo4, phi4](auto part, auto same, int l) constexpr {
+    constexpr int H = decltype(part)::value;
+    for (int p = plo4(H); p < phi4(H); ++p) {
+      const bool ok = !decltype(same)::value || ord4(p) < LOADS_PER_OP / 4;
+      if (ok && l-- == 0) return ord4(p);
+    }
+    return 0;
+  };
+  using Part0 = std::integral_constant<int, 0>;
+  using Part1 = std::integral_constant<int, 1>;
+  using Part2 = std::integral_constant<int, 2>;
+  using Part3 = std::integral_constant<int, 3>;
+  // part h of stage `data`'s loads into ring slot `slot`, back to back
+  auto issue4 = [&](int data, int slot, auto part, auto same) {
+    constexpr int N = pcount4(part, same);
+    char* st = smem + (slot % kStages) * STB;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + data * kRowBytes, a_span);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + data * kRowBytes, b_span);
+#pragma unroll
+    for (int l = 0; l < N; ++l) {
+      const int q = pq4(part, same, l);
+      buffer_load_lds16(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(st + dst_off[q]), int(voff[q]));
+    }
+  };
+  bf16x8_t fsa[4][F], fsb[4][F];
+  // One k-quarter in a fixed instruction order: MFMA m of the 16 on set C;
+  // behind it RP fragment reads (k-quarter rk1 of the stage in ring slot rs1
+  // into set R1, then rk2 of rs2 into R2; a negative set reads nothing); and
+  // the loads of part h of stage ld_data, evenly spaced.  A scheduling
+  // barrier after every step keeps that order.
+  auto q4 = [&](auto C, auto R1, int rs1, int rk1, auto R2, int rs2, int rk2, auto same,
+                auto nloads, int ld_data, auto part, auto reads_per_mfma) {
+    constexpr int CI = decltype(C)::value, RI1 = decltype(R1)::value, RI2 = decltype(R2)::value;
+    constexpr int W1 = RI1 < 0 ? 0 : RI1, W2 = RI2 < 0 ? 0 : RI2;
+    constexpr int V = decltype(nloads)::value, RP = decltype(reads_per_mfma)::value;
+    constexpr int NR = (RI1 >= 0 ? 2 * F : 0) + (RI2 >= 0 ? 2 * F : 0);
+    constexpr int BOFF = decltype(same)::value ? 0 : OPB;
+    const char* st1 = smem + (rs1 % kStages) * STB + frag_off[rk1];
+    const char* st2 = smem + (rs2 % kStages) * STB + frag_off[rk2];
+    char* ldst = smem + (ld_data % kStages) * STB;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    if constexpr (V > 0) {
+      ra = make_rsrc(a_base + ld_data * kRowBytes, a_span);
+      rb = make_rsrc(b_base + ld_data * kRowBytes, b_span);
+    }
+    int l = 0;
+#pragma unroll
+    for (int m = 0; m < F * F; ++m) {
+      const int i = m / F, j = m % F;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fsb[CI][j], fsa[CI][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RP; ++t) {
+        const int r = RP * m + t;
+        if (r < NR) {
+          const bool second = r >= 2 * F;
+          const int rr = second ? r - 2 * F : r;
+          const char* base = second ? st2 : st1;
+          const bf16x8_t v = rr < F ? *reinterpret_cast<const bf16x8_t*>(base + (wm * WT + rr * 32) * kRowBytes)
+                                    : *reinterpret_cast<const bf16x8_t*>(base + BOFF + (wn * WT + (rr - F) * 32) * kRowBytes);
+          if (!second) {
+            if (rr < F) fsa[W1][rr] = v; else fsb[W1][rr - F] = v;
+          } else {
+            if (rr < F) fsa[W2][rr] = v; else fsb[W2][rr - F] = v;
+          }
+        }
+      }
+      if constexpr (V > 0) {
+        if (((m + 1) * V) / (F * F) > (m * V) / (F * F)) {
+          const int q = pq4(part, same, l);
+          buffer_load_lds16(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(ldst + dst_off[q]), int(voff[q]));
+          ++l;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  using Set2 = std::integral_constant<int, 2>;
+  using Set3 = std::integral_constant<int, 3>;
+  using NoSet = std::integral_constant<int, -1>;
+  using NoLoads = std::integral_constant<int, 0>;
+  using OneRead = std::integral_constant<int, 1>;
+  using TwoReads = std::integral_constant<int, 2>;
+  // s_waitcnt lgkmcnt(0), the other counters untouched (gfx9 encoding)
+  auto wait_lgkm0 = []() { __builtin_amdgcn_s_waitcnt(0xC07F); };
+  // workgroup barrier without a memory fence; the signal fences only keep
+  // the compiler from moving memory accesses across it
+  auto plain_barrier = []() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto main_loop4 = [&](auto same) {
+    using S = decltype(same);
+    constexpr int N0 = pcount4(Part0{}, S{});
+    constexpr int N12 = pcount4(Part1{}, S{}) + pcount4(Part2{}, S{});
+    // stage 0 whole and stage 1 but its quarter-0 part; a single stage
+    // loads itself again into the other slot, harmlessly
+    const int d1 = nk > 1 ? 1 : 0;
+    issue4(0, 0, Part1{}, same); issue4(0, 0, Part2{}, same); issue4(0, 0, Part3{}, same); issue4(0, 0, Part0{}, same);
+    issue4(d1, 1, Part1{}, same); issue4(d1, 1, Part2{}, same); issue4(d1, 1, Part3{}, same);
+    wait_vmcnt<N12 + pcount4(Part3{}, S{})>();
+    plain_barrier();
+    // quarters 0 and 1 of stage 0 into sets 0 and 1
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const char* st = smem + frag_off[k];
+#pragma unroll
+      for (int i = 0; i < F; ++i) fsa[k][i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * WT + i * 32) * kRowBytes);
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+        fsb[k][j] = *reinterpret_cast<const bf16x8_t*>(st + (S::value ? 0 : OPB) + (wn * WT + j * 32) * kRowBytes);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto stage4 = [&](int kt, auto last, auto no_ahead) {
+      constexpr bool kLast = decltype(last)::value, kNoAhead = decltype(no_ahead)::value;
+      if constexpr (kLast) {
+        q4(Set0{}, Set2{}, kt, 2, Set3{}, kt, 3, same, NoLoads{}, 0, Part0{}, TwoReads{});
+        q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+        q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+        q4(Set3{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+      } else {
+        // quarter 0: reads of this stage's quarters 2 and 3, last loads of stage kt+1
+        q4(Set0{}, Set2{}, kt, 2, Set3{}, kt, 3, same, std::integral_constant<int, N0>{}, kt + 1, Part0{}, TwoReads{});
+        wait_lgkm0();
+        plain_barrier();                             // ring slot kt is free
+        if constexpr (kNoAhead) {
+          q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+          q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+          wait_vmcnt<0>();
+        } else {
+          q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, std::integral_constant<int, pcount4(Part1{}, S{})>{},
+             kt + 2, Part1{}, TwoReads{});
+          q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, std::integral_constant<int, pcount4(Part2{}, S{})>{},
+             kt + 2, Part2{}, TwoReads{});
+          wait_vmcnt<N12>();
+        }
+        plain_barrier();                             // stage kt+1 has landed
+        if constexpr (kNoAhead)
+          q4(Set3{}, Set0{}, kt + 1, 0, Set1{}, kt + 1, 1, same, NoLoads{}, 0, Part0{}, OneRead{});
+        else
+          q4(Set3{}, Set0{}, kt + 1, 0, Set1{}, kt + 1, 1, same, std::integral_constant<int, pcount4(Part3{}, S{})>{},
+             kt + 2, Part3{}, OneRead{});
+      }
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) stage4(kt, std::false_type{}, std::false_type{});
+    if (kt + 1 < nk) stage4(kt++, std::false_type{}, std::true_type{});
+    stage4(kt, std::true_type{}, std::false_type{});
+  };
+  // the idle wave of a diagonal tile: the same loads, waits and barriers
+  auto idle_loop4 = [&](auto same) {
+    using S = decltype(same);
+    constexpr int N12 = pcount4(Part1{}, S{}) + pcount4(Part2{}, S{});
+    const int d1 = nk > 1 ? 1 : 0;
+    issue4(0, 0, Part1{}, same); issue4(0, 0, Part2{}, same); issue4(0, 0, Part3{}, same); issue4(0, 0, Part0{}, same);
+    issue4(d1, 1, Part1{}, same); issue4(d1, 1, Part2{}, same); issue4(d1, 1, Part3{}, same);
+    wait_vmcnt<N12 + pcount4(Part3{}, S{})>();
+    plain_barrier();
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      issue4(kt + 1, kt + 1, Part0{}, same);
+      plain_barrier();
+      if (kt + 2 < nk) {
+        issue4(kt + 2, kt + 2, Part1{}, same);
+        issue4(kt + 2, kt + 2, Part2{}, same);
+        wait_vmcnt<N12>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      plain_barrier();
+      if (kt + 2 < nk) issue4(kt + 2, kt + 2, Part3{}, same);
+    }
+  };
   const bool idle = T.sym && tm == tn && wm == 1 && wn == 0;
   // a diagonal tile of a matrix times itself: one operand's rows serve both
-  if (T.A == T.B && tm == tn) {
-    if (idle)
-      idle_loop(std::true_type{});
-    else
-      main_loop(std::true_type{});
-  } else if (idle) {
-    idle_loop(std::false_type{});
+  if constexpr (BT == 256) {
+    if (T.A == T.B && tm == tn) {
+      if (idle)
+        idle_loop4(std::true_type{});
+      else
+        main_loop4(std::true_type{});
+    } else if (idle) {
+      idle_loop4(std::false_type{});
+    } else {
+      main_loop4(std::false_type{});
+    }
   } else {
-    main_loop(std::false_type{});
+    if (T.A == T.B && tm == tn) {
+      if (idle)
+        idle_loop(std::true_type{});
+      else
+        main_loop(std::true_type{});
+    } else if (idle) {
+      idle_loop(std::false_type{});
+    } else {
+      main_loop(std::false_type{});
+    }
   }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
