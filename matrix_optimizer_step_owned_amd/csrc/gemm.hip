@@ -16,8 +16,10 @@
 // for L2 reuse).
 //
 // bf16 kernel: BT x BT output tiles (BT = 256 or 128), four waves in a 2 x 2
-// grid, each a (BT/2 x BT/2) block of v_mfma_f32_32x32x16_bf16 fragments with
-// fp32 accumulators.  Operands stream through a two-slot LDS ring of 64-k
+// grid, each a (BT/2 x BT/2) block with fp32 accumulators: 16 x 16 blocks of
+// v_mfma_f32_16x16x32_bf16 for 256-tiles (under the power limit the
+// smaller MFMA runs at a higher clock for the same flops), 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16 for 128-tiles.  Operands stream through a two-slot LDS ring of 64-k
 // stages, filled by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds:
 // lane l of a wave writes bytes 16l..16l+15 of a 1 KB LDS block; the base
 // is a per-operand descriptor in scalar registers, the per-lane offsets are
@@ -25,9 +27,10 @@
 // stage is 128 bytes, one cache line; chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7), which the loads realise by choosing each lane's source
 // address, so that a fragment read (16 rows x one 16-byte chunk per cycle)
-// covers all 64 banks.  A stage runs as four k-quarters of 16 MFMAs per wave.
-// 256-tiles hold four quarters of fragments in registers: a stage's
-// fragments are read within its first quarter and the quarter before, a
+// covers all 64 banks.  A stage runs as four k-quarters of 512 MFMA cycles
+// per wave (32 16x16x32 or 16 32x32x16 MFMAs).  256-tiles hold a whole
+// stage of fragments in registers (two 32-k steps): a stage's fragments are
+// read within its first quarter and the quarter before, a
 // barrier after that quarter frees its ring slot, and the loads of the stage
 // two ahead go into the slot over the following four quarters, most of them
 // in the two quarters without fragment reads; a second barrier after the
@@ -289,6 +292,29 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     for (int j = 0; j < F; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // 256-tiles run v_mfma_f32_16x16x32_bf16 (the same flops for a quarter of
+  // the accumulator traffic per instruction, which under the power limit
+  // runs at a higher clock): F16 x F16 blocks of 16 x 16 per wave.  With the
+  // B fragment first the lane holds row (lane & 15) of a block and, in
+  // register r, column 4 (lane >> 4) + r.
+  constexpr int F16 = WT / 16;
+  f32x4_t acc16[F16][F16];
+  if constexpr (BT == 256) {
+#pragma unroll
+    for (int i = 0; i < F16; ++i)
+#pragma unroll
+      for (int j = 0; j < F16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc16[i][j][r] = 0.f;
+  }
+  // 16 x 16 x 32 fragment read offsets for the two 32-k steps of a stage:
+  // lanes take row lane & 15, chunk 4t + (lane >> 4)
+  int frag16_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = lane & 15;
+    frag16_off[t] = r * kRowBytes + slot_of(r, 4 * t + (lane >> 4)) * 16;
+  }
 
   auto read_frags = [&](int s, int kq, bf16x8_t (&fa)[F], bf16x8_t (&fb)[F], auto same) {
     constexpr int BOFF = decltype(same)::value ? 0 : OPB;
@@ -498,21 +524,21 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       buffer_load_lds16(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(st + dst_off[q]), int(voff[q]));
     }
   };
-  bf16x8_t fsa[4][F], fsb[4][F];
-  // One k-quarter in a fixed instruction order: MFMA m of the 16 on set C;
-  // behind it RP fragment reads (k-quarter rk1 of the stage in ring slot rs1
-  // into set R1, then rk2 of rs2 into R2; a negative set reads nothing); and
-  // the loads of part h of stage ld_data, evenly spaced.  A scheduling
-  // barrier after every step keeps that order.
-  auto q4 = [&](auto C, auto R1, int rs1, int rk1, auto R2, int rs2, int rk2, auto same,
-                auto nloads, int ld_data, auto part, auto reads_per_mfma) {
-    constexpr int CI = decltype(C)::value, RI1 = decltype(R1)::value, RI2 = decltype(R2)::value;
-    constexpr int W1 = RI1 < 0 ? 0 : RI1, W2 = RI2 < 0 ? 0 : RI2;
-    constexpr int V = decltype(nloads)::value, RP = decltype(reads_per_mfma)::value;
-    constexpr int NR = (RI1 >= 0 ? 2 * F : 0) + (RI2 >= 0 ? 2 * F : 0);
+  // fragment set t holds 32-k step t of a stage: F16 A and F16 B blocks
+  bf16x8_t fra[2][F16], frb[2][F16];
+  // One quarter in a fixed instruction order: the 32 MFMAs of half h of the
+  // step in set CS (A blocks 4h..4h+3 by every B block); behind every RS-th
+  // of them one fragment read of the step RSET of the stage in ring slot
+  // rs into set RSET (A blocks, then B blocks; none when RSET < 0); and the
+  // loads of part h of stage ld_data, evenly spaced.  A scheduling barrier
+  // after every MFMA keeps that order.
+  auto q16 = [&](auto cs, auto half, auto rset, int rs, auto rstride, auto same, auto nloads, int ld_data,
+                 auto part) {
+    constexpr int CS = decltype(cs)::value, H = decltype(half)::value, RSET = decltype(rset)::value;
+    constexpr int RS = decltype(rstride)::value, V = decltype(nloads)::value;
     constexpr int BOFF = decltype(same)::value ? 0 : OPB;
-    const char* st1 = smem + (rs1 % kStages) * STB + frag_off[rk1];
-    const char* st2 = smem + (rs2 % kStages) * STB + frag_off[rk2];
+    constexpr int NM = F16 * F16 / 2;                // MFMAs per quarter
+    const char* rst = smem + (rs % kStages) * STB + frag16_off[RSET < 0 ? 0 : RSET];
     char* ldst = smem + (ld_data % kStages) * STB;
     __amdgpu_buffer_rsrc_t ra, rb;
     if constexpr (V > 0) {
@@ -521,27 +547,24 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     }
     int l = 0;
 #pragma unroll
-    for (int m = 0; m < F * F; ++m) {
-      const int i = m / F, j = m % F;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fsb[CI][j], fsa[CI][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < RP; ++t) {
-        const int r = RP * m + t;
-        if (r < NR) {
-          const bool second = r >= 2 * F;
-          const int rr = second ? r - 2 * F : r;
-          const char* base = second ? st2 : st1;
-          const bf16x8_t v = rr < F ? *reinterpret_cast<const bf16x8_t*>(base + (wm * WT + rr * 32) * kRowBytes)
-                                    : *reinterpret_cast<const bf16x8_t*>(base + BOFF + (wn * WT + (rr - F) * 32) * kRowBytes);
-          if (!second) {
-            if (rr < F) fsa[W1][rr] = v; else fsb[W1][rr - F] = v;
-          } else {
-            if (rr < F) fsa[W2][rr] = v; else fsb[W2][rr - F] = v;
-          }
+    for (int m = 0; m < NM; ++m) {
+      const int i = H * (F16 / 2) + m / F16, j = m % F16;
+      // the MFMA in asm with the accumulator as a tied AGPR operand: each
+      // accumulator stays in place (the builtin leaves the register
+      // allocator shuffling the 64 four-register accumulators between AGPR
+      // quads and VGPRs); it touches registers only
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc16[i][j]) : "v"(frb[CS][j]), "v"(fra[CS][i]));
+      if constexpr (RSET >= 0) {
+        if (m % RS == 0 && m / RS < 2 * F16) {
+          const int r = m / RS;
+          if (r < F16)
+            fra[RSET][r] = *reinterpret_cast<const bf16x8_t*>(rst + (wm * WT + r * 16) * kRowBytes);
+          else
+            frb[RSET][r - F16] = *reinterpret_cast<const bf16x8_t*>(rst + BOFF + (wn * WT + (r - F16) * 16) * kRowBytes);
         }
       }
       if constexpr (V > 0) {
-        if (((m + 1) * V) / (F * F) > (m * V) / (F * F)) {
+        if (((m + 1) * V) / NM > (m * V) / NM) {
           const int q = pq4(part, same, l);
           buffer_load_lds16(q < LOADS_PER_OP / 4 ? ra : rb, (LDS_AS void*)(ldst + dst_off[q]), int(voff[q]));
           ++l;
@@ -550,14 +573,14 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  using Set2 = std::integral_constant<int, 2>;
-  using Set3 = std::integral_constant<int, 3>;
+  using Step0 = std::integral_constant<int, 0>;
+  using Step1 = std::integral_constant<int, 1>;
   using NoSet = std::integral_constant<int, -1>;
   using NoLoads = std::integral_constant<int, 0>;
-  using OneRead = std::integral_constant<int, 1>;
-  using TwoReads = std::integral_constant<int, 2>;
+  using Half0 = std::integral_constant<int, 0>;
+  using Half1 = std::integral_constant<int, 1>;
+  using EveryMfma = std::integral_constant<int, 1>;
+  using EverySecond = std::integral_constant<int, 2>;
   // s_waitcnt lgkmcnt(0), the other counters untouched (gfx9 encoding)
   auto wait_lgkm0 = []() { __builtin_amdgcn_s_waitcnt(0xC07F); };
   // workgroup barrier without a memory fence; the signal fences only keep
@@ -579,52 +602,52 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     issue4(d1, 1, Part1{}, same); issue4(d1, 1, Part2{}, same); issue4(d1, 1, Part3{}, same);
     wait_vmcnt<N12 + pcount4(Part3{}, S{})>();
     plain_barrier();
-    // quarters 0 and 1 of stage 0 into sets 0 and 1
+    // step 0 of stage 0 into set 0
+    {
+      const char* st = smem + frag16_off[0];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const char* st = smem + frag_off[k];
+      for (int i = 0; i < F16; ++i) fra[0][i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * WT + i * 16) * kRowBytes);
 #pragma unroll
-      for (int i = 0; i < F; ++i) fsa[k][i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * WT + i * 32) * kRowBytes);
-#pragma unroll
-      for (int j = 0; j < F; ++j)
-        fsb[k][j] = *reinterpret_cast<const bf16x8_t*>(st + (S::value ? 0 : OPB) + (wn * WT + j * 32) * kRowBytes);
+      for (int j = 0; j < F16; ++j)
+        frb[0][j] = *reinterpret_cast<const bf16x8_t*>(st + (S::value ? 0 : OPB) + (wn * WT + j * 16) * kRowBytes);
     }
     __builtin_amdgcn_sched_barrier(0);
-    auto stage4 = [&](int kt, auto last, auto no_ahead) {
+    auto stage16 = [&](int kt, auto last, auto no_ahead) {
       constexpr bool kLast = decltype(last)::value, kNoAhead = decltype(no_ahead)::value;
       if constexpr (kLast) {
-        q4(Set0{}, Set2{}, kt, 2, Set3{}, kt, 3, same, NoLoads{}, 0, Part0{}, TwoReads{});
-        q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
-        q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
-        q4(Set3{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+        q16(Step0{}, Half0{}, Step1{}, kt, EveryMfma{}, same, NoLoads{}, 0, Part0{});
+        q16(Step0{}, Half1{}, NoSet{}, 0, EveryMfma{}, same, NoLoads{}, 0, Part0{});
+        q16(Step1{}, Half0{}, NoSet{}, 0, EveryMfma{}, same, NoLoads{}, 0, Part0{});
+        q16(Step1{}, Half1{}, NoSet{}, 0, EveryMfma{}, same, NoLoads{}, 0, Part0{});
       } else {
-        // quarter 0: reads of this stage's quarters 2 and 3, last loads of stage kt+1
-        q4(Set0{}, Set2{}, kt, 2, Set3{}, kt, 3, same, std::integral_constant<int, N0>{}, kt + 1, Part0{}, TwoReads{});
+        // quarter 0: reads of this stage's step 1, last loads of stage kt+1
+        q16(Step0{}, Half0{}, Step1{}, kt, EveryMfma{}, same, std::integral_constant<int, N0>{}, kt + 1, Part0{});
         wait_lgkm0();
         plain_barrier();                             // ring slot kt is free
         if constexpr (kNoAhead) {
-          q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
-          q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, NoLoads{}, 0, Part0{}, TwoReads{});
+          q16(Step0{}, Half1{}, NoSet{}, 0, EveryMfma{}, same, NoLoads{}, 0, Part0{});
+          q16(Step1{}, Half0{}, NoSet{}, 0, EveryMfma{}, same, NoLoads{}, 0, Part0{});
           wait_vmcnt<0>();
         } else {
-          q4(Set1{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, std::integral_constant<int, pcount4(Part1{}, S{})>{},
-             kt + 2, Part1{}, TwoReads{});
-          q4(Set2{}, NoSet{}, 0, 0, NoSet{}, 0, 0, same, std::integral_constant<int, pcount4(Part2{}, S{})>{},
-             kt + 2, Part2{}, TwoReads{});
+          q16(Step0{}, Half1{}, NoSet{}, 0, EveryMfma{}, same, std::integral_constant<int, pcount4(Part1{}, S{})>{},
+              kt + 2, Part1{});
+          q16(Step1{}, Half0{}, NoSet{}, 0, EveryMfma{}, same, std::integral_constant<int, pcount4(Part2{}, S{})>{},
+              kt + 2, Part2{});
           wait_vmcnt<N12>();
         }
         plain_barrier();                             // stage kt+1 has landed
+        // quarter 3: reads of stage kt+1's step 0
         if constexpr (kNoAhead)
-          q4(Set3{}, Set0{}, kt + 1, 0, Set1{}, kt + 1, 1, same, NoLoads{}, 0, Part0{}, OneRead{});
+          q16(Step1{}, Half1{}, Step0{}, kt + 1, EverySecond{}, same, NoLoads{}, 0, Part0{});
         else
-          q4(Set3{}, Set0{}, kt + 1, 0, Set1{}, kt + 1, 1, same, std::integral_constant<int, pcount4(Part3{}, S{})>{},
-             kt + 2, Part3{}, OneRead{});
+          q16(Step1{}, Half1{}, Step0{}, kt + 1, EverySecond{}, same,
+              std::integral_constant<int, pcount4(Part3{}, S{})>{}, kt + 2, Part3{});
       }
     };
     int kt = 0;
-    for (; kt + 2 < nk; ++kt) stage4(kt, std::false_type{}, std::false_type{});
-    if (kt + 1 < nk) stage4(kt++, std::false_type{}, std::true_type{});
-    stage4(kt, std::true_type{}, std::false_type{});
+    for (; kt + 2 < nk; ++kt) stage16(kt, std::false_type{}, std::false_type{});
+    if (kt + 1 < nk) stage16(kt++, std::false_type{}, std::true_type{});
+    stage16(kt, std::true_type{}, std::false_type{});
   };
   // the idle wave of a diagonal tile: the same loads, waits and barriers
   auto idle_loop4 = [&](auto same) {
@@ -676,6 +699,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
   }
   // no load may still be writing this block's LDS when the block retires
   wait_vmcnt<0>();
+  if constexpr (BT == 256) {
+    // the compiler does not see the asm MFMAs' latency: wait states before
+    // the epilogue reads their accumulators
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  }
 
   // Epilogue.  The ring holds the finished tile as bf16, row-major, 16-byte
   // chunks swizzled per row (stg_swz).  Each lane scales its accumulators
@@ -789,10 +817,50 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
       }
     }
   };
-  if (Y)
-    stage_tile(std::true_type{});
-  else
-    stage_tile(std::false_type{});
+  // 256-tiles: row wm*WT + 16i + (lane & 15), columns wn*WT + 16j + 4(lane >> 4) + 0..3
+  auto stage_tile16 = [&](auto hy) {
+    constexpr bool has_y = decltype(hy)::value;
+    const bool add_gamma = tm == tn && gamma != 0.f && wm == wn;
+    const int cq = lane >> 5;                    // chunk of the 8 columns within a 16-column block
+#pragma unroll
+    for (int i = 0; i < F16; ++i) {
+      const int row = wm * WT + i * 16 + (lane & 15);
+      const int sw = stg_swz(row);
+      char* const srow = stg + row * ROWB + ((lane >> 4) & 1) * 8;
+      const bool diag_row = int64_t(tm) * BT + row < diag_limit;
+#pragma unroll
+      for (int j = 0; j < F16; ++j) {
+        char* const p = srow + ((((wn * WT + j * 16) / 8 + cq) ^ sw) << 4);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = alpha * acc16[i][j][r];
+        if constexpr (has_y) {
+          const uint2 y = *reinterpret_cast<const uint2*>(p);
+          v[0] = fmaf(beta, __uint_as_float(y.x << 16), v[0]);
+          v[1] = fmaf(beta, __uint_as_float(y.x & 0xffff0000u), v[1]);
+          v[2] = fmaf(beta, __uint_as_float(y.y << 16), v[2]);
+          v[3] = fmaf(beta, __uint_as_float(y.y & 0xffff0000u), v[3]);
+        }
+        if (i == j && add_gamma) {               // wm == wn: the tile diagonal
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += ((lane & 15) == 4 * (lane >> 4) + r && diag_row) ? gamma : 0.f;
+        }
+        *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);         // bounds the live accumulator copies
+    }
+  };
+  if constexpr (BT == 256) {
+    if (Y)
+      stage_tile16(std::true_type{});
+    else
+      stage_tile16(std::false_type{});
+  } else {
+    if (Y)
+      stage_tile(std::true_type{});
+    else
+      stage_tile(std::false_type{});
+  }
   lds_barrier();
 
   // 8 x 4 block transposes: lane tq takes rows 8rb..8rb+7 of columns
