@@ -472,10 +472,11 @@ gemm_bf16_kernel(const GemmTask* __restrict__ tasks, const TileRef* __restrict__
     }
   };
 
-  // 256-tiles: four fragment sets, two barriers per stage.  Set k holds
-  // k-quarter k of a stage.  Stage s+1's quarters 0 and 1 are read during
-  // quarter 3 of stage s (one read behind each MFMA), its quarters 2 and 3
-  // during its own quarter 0 (two behind each of the first eight MFMAs).
+  // 256-tiles: a whole stage of fragments in registers, two barriers per
+  // stage.  Fragment set t holds 32-k step t of a stage; a quarter is half a
+  // step (32 MFMAs).  Stage s+1's step 0 is read during quarter 3 of stage s
+  // (one read behind every second MFMA), its step 1 during its own quarter 0
+  // (one behind each of the first sixteen MFMAs).
   // After quarter 0 a barrier frees the ring slot of stage s, and stage
   // s+2's 16 loads per wave go into it: 6 in quarter 1, 6 in quarter 2, 2 in
   // quarter 3, 2 in quarter 0 of stage s+1, evenly spaced within each
