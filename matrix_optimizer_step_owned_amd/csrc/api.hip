@@ -1074,7 +1074,8 @@ const char* dmuon_backend_info(void) {
     std::ostringstream os;
     os << "{\"arch\": \"gfx950\", "
        << "\"ns_gemm_bf16\": {\"kernel\": \"gemm_bf16_kernel\", \"tiles\": [" << kTileBf16 << ", " << kTileBf16Big
-       << "], \"waves\": 4, \"mfma\": \"v_mfma_f32_32x32x16_bf16\", \"accumulate\": \"f32\", "
+       << "], \"waves\": 4, \"mfma\": {\"" << kTileBf16 << "\": \"v_mfma_f32_32x32x16_bf16\", \""
+       << kTileBf16Big << "\": \"v_mfma_f32_16x16x32_bf16\"}, \"accumulate\": \"f32\", "
        << "\"stage_k\": 64, \"lds_stages\": 2, \"operand_loads\": \"buffer_load_dwordx4 to LDS\", "
        << "\"big_tile_rule\": {\"min_first_stage_tiles\": " << kBigTileMinCount
        << ", \"min_wide_share\": 0.5, \"wide_min_dim\": " << kBigTileMinDim

@@ -236,7 +236,9 @@ def test_backend_info_describes_the_plan(dm, monkeypatch):
     monkeypatch.delenv("DMUON_GEMM_TILE", raising=False)
     monkeypatch.delenv("DMUON_GEMM_TILE_F32", raising=False)
     info = dm.dmuon_backend_info()
-    assert info["ns_gemm_bf16"]["mfma"] == "v_mfma_f32_32x32x16_bf16"
+    tiles = info["ns_gemm_bf16"]["tiles"]
+    assert info["ns_gemm_bf16"]["mfma"] == {str(tiles[0]): "v_mfma_f32_32x32x16_bf16",
+                                            str(tiles[1]): "v_mfma_f32_16x16x32_bf16"}
     assert info["ns_gemm_f32"]["mfma"] == "v_mfma_f32_32x32x2f32"
     batches = [[(m.rows, m.cols) for m in di.workload(k).matrices] for k in range(5)]
     batches += [[(3072, 8192)], [(1024, 1024)] * 16, [(4096, 4096)], [(128, 2048)] * 40,
