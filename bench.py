@@ -379,9 +379,12 @@ def main():
     peak = PEAK_BF16_TFLOPS if args.ns_precision == "bf16" else PEAK_F32_TFLOPS
     flops_step = nominal_flops(shapes, hp["ns_steps"])
 
+    power = PowerSampler()
+
     def timed_run(hp_run, copy_after=False):
         """Warm-up steps, then the timed steps of one configuration; returns
-        (ms per step, per-kernel profile, wall seconds)."""
+        (ms per step, per-kernel profile, wall seconds); the board power over
+        the timed steps is left in timed_run.power."""
         ws_bytes = dm.dmuon_step_workspace_size(params, grad_sets[0], moms, **hp_run)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -395,6 +398,7 @@ def main():
         end = torch.cuda.Event(enable_timing=True)
         dm.dmuon_profile_begin()
         torch.cuda.synchronize()
+        power.start()
         t0 = time.perf_counter()
         start.record(stream)
         for s in range(args.steps):
@@ -402,6 +406,7 @@ def main():
         end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        timed_run.power = power.stop()
         prof = dm.dmuon_profile_end()["kernels"]
         if copy_after:
             copy_probe(dev)
@@ -430,6 +435,7 @@ def main():
         return ns_ms, alg_flops, dom_name, dom, achieved
 
     ms_step, prof, wall = timed_run(hp, copy_after=args.copy_probe)
+    power_main = timed_run.power
     value = flops_step / (ms_step * 1e-3) / 1e12
     ns_ms, alg_flops, dom_name, dom, achieved = gemm_summary(prof)
     # the committed counter summaries cover the default configuration only
@@ -485,6 +491,8 @@ def main():
             "executed_tflops": counted / (ns_ms * 1e-3) / 1e12,
             "frac_of_peak": counted / (ns_ms * 1e-3) / 1e12 / peak,
             "summary": os.path.relpath(MFMA_SUMMARY, ROOT)},
+        # board power and clock over the timed steps (the GEMMs run at the power cap)
+        "power": power_main,
     }
     if default_cfg and not args.no_standard_form:
         # the headline configuration names both NS forms: time the standard form too
@@ -499,11 +507,60 @@ def main():
             "roofline": {"bound": "mfma", "kernel": dom_name_s, "achieved": ach_s, "peak": peak,
                          "unit": "TFLOP/s", "frac": ach_s / peak,
                          "mean_launch_ms": dom_s["ms"] / dom_s["launches"]},
-            "gram_speedup": ms_std / ms_step}
+            "gram_speedup": ms_std / ms_step, "power": timed_run.power}
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, hp)
     print(json.dumps(out), flush=True)
+
+
+class PowerSampler:
+    """Board power and graphics clock, read through amdsmi (read-only queries)
+    every 50 ms on a thread of its own while the timed steps run; the summary
+    is None where amdsmi is not available."""
+
+    def __init__(self):
+        self.handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.amdsmi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.cap_w = amdsmi.amdsmi_get_power_cap_info(self.handle)["power_cap"] / 1e6
+        except Exception:
+            self.handle = None
+
+    def start(self):
+        import threading
+        self.samples = []
+        if self.handle is None:
+            return
+        self.stop_flag = threading.Event()
+
+        def run():
+            while not self.stop_flag.is_set():
+                try:
+                    m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+                    self.samples.append((m.get("current_socket_power"), m.get("current_gfxclk")))
+                except Exception:
+                    pass
+                time.sleep(0.05)
+
+        self.thread = threading.Thread(target=run, daemon=True)
+        self.thread.start()
+
+    def stop(self):
+        if self.handle is None:
+            return None
+        self.stop_flag.set()
+        self.thread.join()
+        pw = sorted(p for p, _ in self.samples if isinstance(p, (int, float)))
+        ck = sorted(c for _, c in self.samples if isinstance(c, (int, float)))
+        if not pw:
+            return None
+        return {"socket_w_median": pw[len(pw) // 2], "socket_w_max": pw[-1], "cap_w": self.cap_w,
+                "gfxclk_mhz_median": ck[len(ck) // 2] if ck else None, "samples": len(pw),
+                "source": "amdsmi gpu metrics, sampled every 50 ms over the timed steps"}
 
 
 def copy_probe(dev):
