@@ -512,3 +512,18 @@ def test_fused_clip_entry_points_reject_null(dm):
     assert lib.dmuon_clip_coefficients(arr, 1, 1, mx, 2.0, None, None, 1 << 42, 1 << 20, None) == \
         dm.DMUON_ERR_INVALID_ARG
     assert "coef_out" in dm.dmuon_last_error()
+
+
+def test_bench_power_sampler_without_a_gpu():
+    """The benchmark's board-power sampler reports None, and does not raise,
+    where amdsmi or a GPU is not available (as in this container)."""
+    import time
+    import bench
+    p = bench.PowerSampler()
+    p.start()
+    time.sleep(0.1)
+    summary = p.stop()
+    if p.handle is None:
+        assert summary is None
+    else:       # a box with a GPU: the summary carries the readings
+        assert summary is None or {"socket_w_median", "cap_w", "gfxclk_mhz_median"} <= set(summary)
